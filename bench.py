@@ -1,0 +1,193 @@
+#!/usr/bin/env python3
+"""Throughput of the low-bit routed-expert MoE layer on one MI355X.
+
+One step = the whole layer on one batch: moe_route -> moe_permute -> moe_expert_ffn (its
+stages: prepare, FC1 + SwiGLU, FC2) -> moe_combine, on synthetic seeded inputs that are
+already resident in HBM.  Default workload: the decode layer (384 experts, top-8, hidden
+4096, intermediate 2048, 2-bit codebook weights with group-32 bf16 scales, Zipf-skewed
+routing) at T = 64 tokens.
+
+Every step is timed with HIP events on the stream the kernels run on; the last-level
+caches are flushed between steps (outside the events) by writing a 1 GiB buffer, so the
+expert weights come from HBM.  The FC1 kernel (2/3 of the weight bytes) is the dominant
+kernel: its algorithmic bytes (packed weights of the experts that received tokens, x read
+once, h written once) divided by its event-timed duration give `roofline.achieved`.
+
+Prints one JSON line.  `--gpus` above 1 is refused: this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def weight_bytes_per_expert(sp: dict, which: int) -> int:
+    """Packed bytes (codes + scales) of one expert's W1 (which=1) or W2 (which=2)."""
+    H, I = sp["H"], sp["I"]
+    n = 2 * I * H if which == 1 else H * I
+    if sp["fmt"] == "w2":
+        return n // 4 + (n // 32) * 2
+    return n * 3 // 8 + n // 64
+
+
+def cpu_baseline(sp, batch, T, n_tok):
+    """The oracle, as it stands, on the first n_tok tokens of the same batch."""
+    import numpy as np
+
+    from oracle import moe as OM
+    import moegen
+
+    logits, x = batch["logits"][:n_tok], batch["x"][:n_tok]
+    ids, _ = OM.route(logits, sp["k"])
+    used = sorted(set(ids.reshape(-1).tolist()))
+    # only the experts the sample routes to are materialised for the oracle
+    arrays = {}
+    for e in used:
+        for key, a in moegen.expert(sp, e).items():
+            arrays.setdefault(key, {})[e] = a
+    full = {key: np.zeros((sp["E"],) + next(iter(d.values())).shape, next(iter(d.values())).dtype)
+            for key, d in arrays.items()}
+    for key, d in arrays.items():
+        for e, a in d.items():
+            full[key][e] = a
+    lay = OM.Layer(sp["fmt"], full)
+    t0 = time.perf_counter()
+    OM.layer_forward(lay, logits, x, sp["k"])
+    dt = time.perf_counter() - t0
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return {"value": n_tok / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n_tok} of the {T} tokens ({len(used)} experts), numpy fp64, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layer", default="decode", help="decode | tiny")
+    ap.add_argument("--T", type=int, default=64)
+    ap.add_argument("--no-flush", action="store_true", help="do not flush caches between steps")
+    ap.add_argument("--cpu-tokens", type=int, default=4, help="tokens of the oracle's timed sample (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this MoE layer path runs on one GPU; --gpus above 1 is not supported "
+              "(the multi-GPU split is described in DESIGN.md, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moegen
+    from bit_moe_expert_top_amd import _lib as L
+
+    sp = moegen.spec(args.layer)
+    T, k, E, H, I = args.T, sp["k"], sp["E"], sp["H"], sp["I"]
+    print(f"[bench] generating layer {args.layer} (E={E} k={k} H={H} I={I} {sp['fmt']}), T={T}",
+          file=sys.stderr, flush=True)
+    arrays = moegen.weights(sp)
+    dw = L.DeviceWeights({"w2": 1, "w3": 2}[sp["fmt"]], E, H, I, arrays)
+    batch = moegen.batch(sp, T)
+    dev = torch.device("cuda")
+    logits = torch.from_numpy(batch["logits"]).to(dev)
+    x = torch.from_numpy(batch["x"].view(np.int16)).to(dev)
+    R = T * k
+    i32 = dict(dtype=torch.int32, device=dev)
+    ids = torch.empty((T, k), **i32)
+    gw = torch.empty((T, k), dtype=torch.float32, device=dev)
+    counts, offsets = torch.empty(E, **i32), torch.empty(E + 1, **i32)
+    perm, inv = torch.empty(R, **i32), torch.empty(R, **i32)
+    ws_p = torch.empty(max(1, L.moe_permute_ws_bytes(T, k, E)), dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(max(1, L.moe_expert_ffn_ws_bytes(dw, T, k)), dtype=torch.uint8, device=dev)
+    y = torch.empty((R, H), dtype=torch.float32, device=dev)
+    out = torch.empty((T, H), dtype=torch.int16, device=dev)
+    n_stages = L.moe_expert_ffn_num_stages(dw, T, k)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def step(evs=None):
+        if evs:
+            evs[0].record(stream)
+        L.moe_route(logits, k, ids, gw)
+        L.moe_permute(ids, E, ws=ws_p, out=(counts, offsets, perm, inv))
+        for s in range(n_stages):
+            if evs:
+                evs[1 + 2 * s].record(stream)
+            L.moe_expert_ffn_stage(dw, x, k, counts, offsets, perm, y, ws_f, s)
+            if evs:
+                evs[2 + 2 * s].record(stream)
+        L.moe_combine(y, inv, gw, out_fp32=False, out=out)
+        if evs:
+            evs[-1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    n_active = int((counts > 0).sum().item())
+    print(f"[bench] {n_active} experts active; timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    all_evs = [[ev() for _ in range(2 + 2 * n_stages)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if not args.no_flush:
+            flush.zero_()
+        step(all_evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    step_ms = [e[0].elapsed_time(e[-1]) for e in all_evs]
+    stage_ms = [[e[1 + 2 * s].elapsed_time(e[2 + 2 * s]) for e in all_evs] for s in range(n_stages)]
+    ms = float(np.mean(step_ms))
+    fc1_ms = float(np.mean(stage_ms[1]))
+    fc2_ms = float(np.mean(stage_ms[2]))
+    w1b = n_active * weight_bytes_per_expert(sp, 1)
+    w2b = n_active * weight_bytes_per_expert(sp, 2)
+    fc1_bytes = w1b + T * H * 2 + R * I * 2
+    fc1_gbs = fc1_bytes / (fc1_ms * 1e-3) / 1e9
+    weight_gbs = (w1b + w2b) / ((fc1_ms + fc2_ms) * 1e-3) / 1e9
+
+    res = {
+        "metric": "MoE-layer tokens/sec (decode; weight HBM GB/s of the expert kernels in roofline)",
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; uniform 2-bit codes, bf16 group-32 scales, N(0,1) x, Zipf s=1.1 logits)",
+        "config": {"workload": f"{args.layer} MoE layer E={E} top-{k} H={H} I={I} {sp['fmt']} T={T}",
+                   "tokens": T, "experts_active": n_active, "cache_flush_between_steps": not args.no_flush},
+        "roofline": {"bound": "hbm", "kernel": "FC1 + SwiGLU (w2_stream_kernel<1>)",
+                     "achieved": fc1_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": fc1_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "alg_bytes_per_launch": fc1_bytes, "avg_launch_ms": fc1_ms},
+        "stages_ms": {"route+permute+prepare+combine": ms - fc1_ms - fc2_ms, "fc1": fc1_ms, "fc2": fc2_ms},
+        "weight_GBps_fc1_fc2": weight_gbs,
+        "wall_s_timed_loop_incl_flush": wall,
+    }
+    if args.cpu_tokens > 0:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(sp, batch, T, min(args.cpu_tokens, T))
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,212 @@
+"""ctypes binding of ``libbitmoe.so`` (the C ABI in ``include/bitmoe.h``).
+
+Argument marshalling only: torch tensors supply device memory and the current HIP stream;
+every step of the layer runs in the library's kernels.  There is no fallback: if the
+library is not built, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbitmoe.so")
+
+MOE_FMT_W2, MOE_FMT_W3, MOE_FMT_MXFP4 = 1, 2, 3
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m bit_moe_expert_top_amd.build`")
+lib = ctypes.CDLL(LIB_PATH)
+
+_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+
+
+class MoeWeights(ctypes.Structure):
+    _fields_ = [
+        ("E", _i32), ("H", _i32), ("I", _i32), ("fmt", _i32),
+        ("w1_codes", _p), ("w1_scales", _p), ("w2_codes", _p), ("w2_scales", _p),
+        ("n_hot", _i32), ("hot_ids", _p),
+        ("hot_w1_codes", _p), ("hot_w1_scales", _p), ("hot_w2_codes", _p), ("hot_w2_scales", _p),
+    ]
+
+
+_SIGS = {
+    "moe_route": (_i32, [_p, _i32, _i32, _i32, _p, _p, _p]),
+    "moe_permute_ws_bytes": (_sz, [_i32, _i32, _i32]),
+    "moe_permute": (_i32, [_p, _i32, _i32, _i32, _p, _p, _p, _p, _p, _sz, _p]),
+    "moe_expert_ffn_ws_bytes": (_sz, [ctypes.POINTER(MoeWeights), _i32, _i32, _i32]),
+    "moe_expert_ffn": (_i32, [ctypes.POINTER(MoeWeights), _p, _i32, _i32, _p, _p, _p, _p, _p, _sz, _p]),
+    "moe_expert_ffn_num_stages": (_i32, [ctypes.POINTER(MoeWeights), _i32, _i32]),
+    "moe_expert_ffn_stage": (_i32, [ctypes.POINTER(MoeWeights), _p, _i32, _i32, _p, _p, _p, _p, _p, _sz, _i32,
+                                    _p]),
+    "moe_combine": (_i32, [_p, _p, _p, _i32, _i32, _i32, _p, _i32, _p]),
+    "moe_mxfp4_to_fp8": (_i32, [_p, _p, _i64, _i32, _p, _p, _p]),
+    "moe_mxfp8_quantize": (_i32, [_p, _i64, _i32, _p, _p, _p]),
+    "moe_debug_dequant": (_i32, [ctypes.POINTER(MoeWeights), _i32, _i32, _p, _p]),
+    "moe_status_str": (ctypes.c_char_p, [_i32]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {lib.moe_status_str(status).decode()} ({status})")
+        self.status = status
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise MoeError(fn, status)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t: torch.Tensor, dtype, name: str):
+    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous {dtype} tensor on the GPU")
+
+
+# --------------------------------------------------------------------- weights
+class DeviceWeights:
+    """Device copies of one layer's packed experts and the ``moe_weights`` struct that points
+    at them (the tensors are kept alive by this object)."""
+
+    def __init__(self, fmt: int, E: int, H: int, I: int, arrays: dict, device="cuda"):
+        def t(a):
+            return torch.from_numpy(a.view(_np_uint_as_int(a.dtype))).to(device) if a is not None else None
+
+        self.fmt, self.E, self.H, self.I = fmt, E, H, I
+        self.t = {key: t(a) for key, a in arrays.items() if a is not None and a.size > 0}
+        hot = self.t.get("hot_ids")
+        self.n_hot = 0 if hot is None else int(hot.numel())
+        g = lambda key: _ptr(self.t.get(key))
+        self.c = MoeWeights(E, H, I, fmt, g("w1_codes"), g("w1_scales"), g("w2_codes"), g("w2_scales"),
+                            self.n_hot, g("hot_ids"), g("hot_w1_codes"), g("hot_w1_scales"),
+                            g("hot_w2_codes"), g("hot_w2_scales"))
+
+
+def _np_uint_as_int(dt):
+    import numpy as np
+
+    return {np.dtype(np.uint32): np.int32, np.dtype(np.uint16): np.int16, np.dtype(np.uint8): np.uint8,
+            np.dtype(np.int32): np.int32}[np.dtype(dt)]
+
+
+# --------------------------------------------------------------------- the four calls
+def moe_route(logits: torch.Tensor, k: int, topk_ids=None, topk_w=None):
+    _dev(logits, torch.float32, "logits")
+    T, E = logits.shape
+    topk_ids = torch.empty((T, k), dtype=torch.int32, device=logits.device) if topk_ids is None else topk_ids
+    topk_w = torch.empty((T, k), dtype=torch.float32, device=logits.device) if topk_w is None else topk_w
+    _check("moe_route", lib.moe_route(_ptr(logits), T, E, k, _ptr(topk_ids), _ptr(topk_w), _stream()))
+    return topk_ids, topk_w
+
+
+def moe_permute_ws_bytes(T: int, k: int, E: int) -> int:
+    return lib.moe_permute_ws_bytes(T, k, E)
+
+
+def moe_permute(topk_ids: torch.Tensor, E: int, ws=None, out=None):
+    _dev(topk_ids, torch.int32, "topk_ids")
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    if out is None:
+        out = (torch.empty(E, dtype=torch.int32, device=dev), torch.empty(E + 1, dtype=torch.int32, device=dev),
+               torch.empty(T * k, dtype=torch.int32, device=dev), torch.empty(T * k, dtype=torch.int32, device=dev))
+    counts, offsets, perm, inv = out
+    need = moe_permute_ws_bytes(T, k, E)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    nbytes = 0 if ws is None else ws.numel()
+    _check("moe_permute", lib.moe_permute(_ptr(topk_ids), T, k, E, _ptr(counts), _ptr(offsets), _ptr(perm),
+                                          _ptr(inv), _ptr(ws), nbytes, _stream()))
+    return counts, offsets, perm, inv
+
+
+def moe_expert_ffn_ws_bytes(w: DeviceWeights, T: int, k: int, fp8_slots: int = 0) -> int:
+    return lib.moe_expert_ffn_ws_bytes(ctypes.byref(w.c), T, k, fp8_slots)
+
+
+def moe_expert_ffn(w: DeviceWeights, x: torch.Tensor, k: int, counts, offsets, perm, y_perm=None, ws=None,
+                   fp8_slots: int | None = None):
+    _dev(x, torch.int16, "x (bf16 bits as int16)")
+    T = x.shape[0]
+    if y_perm is None:
+        y_perm = torch.empty((T * k, w.H), dtype=torch.float32, device=x.device)
+    if ws is None:
+        slots = w.n_hot if fp8_slots is None else fp8_slots
+        ws = torch.empty(max(1, moe_expert_ffn_ws_bytes(w, T, k, slots)), dtype=torch.uint8, device=x.device)
+    _check("moe_expert_ffn", lib.moe_expert_ffn(ctypes.byref(w.c), _ptr(x), T, k, _ptr(counts), _ptr(offsets),
+                                                _ptr(perm), _ptr(y_perm), _ptr(ws), ws.numel(), _stream()))
+    return y_perm
+
+
+def moe_expert_ffn_num_stages(w: DeviceWeights, T: int, k: int) -> int:
+    return lib.moe_expert_ffn_num_stages(ctypes.byref(w.c), T, k)
+
+
+def moe_expert_ffn_stage(w: DeviceWeights, x: torch.Tensor, k: int, counts, offsets, perm, y_perm, ws,
+                         stage: int):
+    T = x.shape[0]
+    _check("moe_expert_ffn_stage", lib.moe_expert_ffn_stage(ctypes.byref(w.c), _ptr(x), T, k, _ptr(counts),
+                                                            _ptr(offsets), _ptr(perm), _ptr(y_perm), _ptr(ws),
+                                                            ws.numel(), stage, _stream()))
+
+
+def moe_combine(y_perm: torch.Tensor, inv: torch.Tensor, topk_w: torch.Tensor, out_fp32: bool = False,
+                out=None):
+    T, k = topk_w.shape
+    H = y_perm.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32 if out_fp32 else torch.int16, device=y_perm.device)
+    _check("moe_combine", lib.moe_combine(_ptr(y_perm), _ptr(inv), _ptr(topk_w), T, k, H, _ptr(out),
+                                          1 if out_fp32 else 0, _stream()))
+    return out
+
+
+def moe_mxfp4_to_fp8(codes: torch.Tensor, scales: torch.Tensor):
+    rows, half = codes.shape
+    K = 2 * half
+    elems = torch.empty((rows, K), dtype=torch.uint8, device=codes.device)
+    sc = torch.empty((rows, K // 32), dtype=torch.uint8, device=codes.device)
+    _check("moe_mxfp4_to_fp8", lib.moe_mxfp4_to_fp8(_ptr(codes), _ptr(scales), rows, K, _ptr(elems), _ptr(sc),
+                                                    _stream()))
+    return elems, sc
+
+
+def moe_mxfp8_quantize(x: torch.Tensor):
+    rows, K = x.shape
+    elems = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
+    sc = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device)
+    _check("moe_mxfp8_quantize", lib.moe_mxfp8_quantize(_ptr(x), rows, K, _ptr(elems), _ptr(sc), _stream()))
+    return elems, sc
+
+
+def moe_debug_dequant(w: DeviceWeights, e: int, which: int):
+    rows, K = (2 * w.I, w.H) if which == 1 else (w.H, w.I)
+    out = torch.empty((rows, K), dtype=torch.float32, device="cuda")
+    _check("moe_debug_dequant", lib.moe_debug_dequant(ctypes.byref(w.c), e, which, _ptr(out), _stream()))
+    return out
+
+
+def layer_forward(w: DeviceWeights, logits: torch.Tensor, x: torch.Tensor, k: int, out_fp32: bool = True):
+    """The four calls in order; returns every intermediate (for tests and the bench)."""
+    ids, gw = moe_route(logits, k)
+    counts, offsets, perm, inv = moe_permute(ids, w.E)
+    y = moe_expert_ffn(w, x, k, counts, offsets, perm)
+    out = moe_combine(y, inv, gw, out_fp32=out_fp32)
+    return dict(ids=ids, gates=gw, counts=counts, offsets=offsets, perm=perm, inv=inv, y_perm=y, out=out)

@@ -1,0 +1,54 @@
+// Host-side launchers of the gfx950 kernels (internal to the library; the public C ABI is
+// include/bitmoe.h).  Each returns hipSuccess or the launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bitmoe {
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                        hipStream_t s);
+
+// Rows per block of the multi-block grouping path; R <= kPermuteChunk uses one block.
+constexpr int kPermuteChunk = 4096;
+size_t permute_ws_bytes(int64_t R, int E);
+hipError_t launch_permute(const int32_t* ids, int R, int E, int32_t* counts, int32_t* offsets,
+                          int32_t* perm, int32_t* inv, void* ws, hipStream_t s);
+
+// Fill with a kernel rather than hipMemsetAsync, so the calls stay graph-capture friendly.
+hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
+
+hipError_t launch_combine(const float* y, const int32_t* inv, const float* w, int T, int k, int H,
+                          void* out, bool out_f32, hipStream_t s);
+
+// ---- expert FFN (low-bit formats)
+struct LowbitWeights {
+  int fmt;  // 1 = 2-bit codebook, 2 = 3-bit
+  const void* w1_codes;
+  const void* w1_scales;
+  const void* w2_codes;
+  const void* w2_scales;
+};
+
+// Work list of grouped-row chunks built on the device from `offsets`.
+//   int32 header[4]: [0] = number of chunks; then int4 items {expert, first row, rows, 0}.
+size_t plan_bytes(int64_t max_items);
+// One launch: the work list, and (if xp) x stored in the k-slot order of the MFMA operand.
+hipError_t launch_prepare(const int32_t* offsets, int E, int chunk_rows, const int32_t* hot_ids,
+                          int n_hot, bool want_hot, int32_t* plan, const uint16_t* x, int T, int H,
+                          uint16_t* xp, hipStream_t s);
+
+// Decode-style kernels: weight-streaming, MFMA on 16-token tiles.
+hipError_t launch_lowbit_fc1(const LowbitWeights& w, int E, int H, int I, int k,
+                             const uint16_t* xp, const int32_t* perm, const int32_t* plan,
+                             int max_items, int nt, uint16_t* hbuf, hipStream_t s);
+hipError_t launch_lowbit_fc2(const LowbitWeights& w, int E, int H, int I,
+                             const uint16_t* hbuf, const int32_t* plan, int max_items, int nt,
+                             float* y, hipStream_t s);
+
+hipError_t launch_debug_dequant(const LowbitWeights& w, int E, int H, int I, int e, int which,
+                                float* out, hipStream_t s);
+
+}  // namespace bitmoe

@@ -1,0 +1,190 @@
+/*
+ * bitmoe.h -- C ABI of the low-bit routed-expert MoE FFN for AMD MI355X (gfx950).
+ *
+ * One MoE layer is four calls, in this order, all enqueued on one HIP stream:
+ *
+ *   moe_route      router logits            -> top-k expert ids and gates
+ *   moe_permute    expert ids               -> per-expert counts/offsets, grouping perm/inv
+ *   moe_expert_ffn tokens + grouped rows    -> FC1 + SwiGLU + FC2 of each row's expert
+ *   moe_combine    expert outputs + gates   -> one output row per token
+ *
+ * Sources, by page title and section:
+ *   [Moet-QA]      mhpn.cn Q&A on the vLLM-Moet project (2-bit experts on the sign-symmetric
+ *                  codebook {-4,-1,1,4}; the FP4 set of hot experts).
+ *   [Moet-README]  ossradar.top page "vLLM-Moet": release notes of v2026.11.03-r23 (the prefill
+ *                  MoE as FC1 + SwiGLU + MXFP8 quantisation, then FC2) and the README tables
+ *                  (routed experts, MXFP4 checkpoint, graph-captured decode step).
+ *   [Strata-R9700] lcz.me thread on porting Strata to the R9700, path 6 (3-bit experts: eight
+ *                  levels, e4m3 scale / 64, 32 codes in three 32-bit words).
+ *   [Day0-MXFP4]   ruibaoantu.com article on a day-0 MoE port, section 4 (MXFP4 experts
+ *                  converted online to FP8 in a reused workspace) and section 5 (the conversion
+ *                  workspace kept apart from other buffers).
+ *   [OCP-MX]       OCP Microscaling Formats v1.0 (e8m0, e2m1, e4m3fn, the MX scale rule).
+ *
+ * Conventions shared by every call:
+ *   - Every pointer argument is a DEVICE pointer owned by the caller, except `moe_weights*`
+ *     itself (a host struct whose members are device pointers).  The library allocates no
+ *     device memory and keeps no mutable global state; scratch lives in the caller's `ws`.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Calls only
+ *     enqueue work and never synchronise the host, so a layer can be captured in a HIP graph.
+ *   - Argument errors are detected on the host and returned before anything is enqueued.
+ *     A failed launch returns MOE_ERR_HIP.  Faults inside kernels surface, as usual in HIP,
+ *     at the caller's next synchronisation.
+ *   - T = 0 is valid for every call and enqueues nothing.
+ *   - Inputs are trusted to be finite (NaN router logits are the caller's error).
+ *
+ * Shapes: T tokens, E experts, k experts per token (1 <= k <= E <= 1024), H hidden size,
+ * I expert intermediate size, R = T*k routed rows.  All arrays are row-major.
+ */
+#ifndef BITMOE_H
+#define BITMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, bad size or shape, k out of range        */
+  MOE_ERR_UNSUPPORTED = -2, /* a valid request this build does not implement            */
+  MOE_ERR_WORKSPACE = -3,   /* ws_bytes smaller than the matching *_ws_bytes() query    */
+  MOE_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed                */
+} moe_status;
+
+/* Expert weight formats.  Every format stores the reduction dimension K contiguously:
+ * W1 is [2I][H] per expert (rows [0,I) = gate projection, rows [I,2I) = up projection),
+ * W2 is [H][I] per expert.  Scales group consecutive weights along K inside one row.
+ *
+ *  MOE_FMT_W2    [Moet-QA] 2-bit codebook: codes u32[rows][K/16], code i of a word at bits
+ *                [2i, 2i+2), code c -> level {-4,-1,1,4}[c]; scales bf16 (u16 bits)
+ *                [rows][K/32]; weight = level * scale.  K % 256 == 0.
+ *                Precondition: scales are normal bf16 numbers with |scale| < 2^125 (then the
+ *                decoded weights are exact bf16 values; a zero or subnormal scale decodes the
+ *                +-4 levels within 2^-124 of the exact value).
+ *  MOE_FMT_W3    [Strata-R9700] 3-bit, 8 levels: codes u32[rows][K/32*3], the three words of a
+ *                group of 32 codes form one little-endian 96-bit field and code i sits at bits
+ *                [3i, 3i+3); code c -> level {-8,-5,-3,-1,1,3,5,8}[c]; scales e4m3fn bytes
+ *                [rows][K/64]; weight = level * e4m3(scale) / 64.  K % 256 == 0.
+ *  MOE_FMT_MXFP4 [OCP-MX] e2m1 elements, codes u8[rows][K/2] (element 2i in the low nibble),
+ *                e8m0 scale bytes [rows][K/32]; weight = e2m1 * 2^(scale-127).  Hot set only.
+ */
+typedef enum { MOE_FMT_W2 = 1, MOE_FMT_W3 = 2, MOE_FMT_MXFP4 = 3 } moe_wfmt;
+
+/* One layer's experts.  Every expert not in the hot set uses `fmt` (W2 or W3); its arrays
+ * are stacked along a leading [E] axis.  A hot expert ([Moet-QA]: the hottest experts are
+ * kept at FP4 precision) is held in MXFP4 instead: its MXFP4 arrays are stacked along
+ * [n_hot] in the order of `hot_ids`, and its slot in the low-bit arrays is never read. */
+typedef struct {
+  int32_t E, H, I;
+  int32_t fmt;                 /* MOE_FMT_W2 or MOE_FMT_W3                                   */
+  const void* w1_codes;        /* [E][2I][...] low-bit codes of W1                           */
+  const void* w1_scales;       /* [E][2I][...] scales of W1                                  */
+  const void* w2_codes;        /* [E][H][...]  codes of W2                                   */
+  const void* w2_scales;       /* [E][H][...]  scales of W2                                  */
+  int32_t n_hot;               /* number of experts held in MXFP4 (0 = none)                 */
+  const int32_t* hot_ids;      /* device int32[n_hot], distinct expert ids (NULL if n_hot=0) */
+  const void* hot_w1_codes;    /* [n_hot][2I][H/2]  u8                                       */
+  const void* hot_w1_scales;   /* [n_hot][2I][H/32] u8 e8m0                                  */
+  const void* hot_w2_codes;    /* [n_hot][H][I/2]   u8                                       */
+  const void* hot_w2_scales;   /* [n_hot][H][I/32]  u8 e8m0                                  */
+} moe_weights;
+
+/* moe_route -- top-k routing ([Moet-README]: each token is served by k routed experts).
+ *   logits    f32[T][E]   router logits
+ *   topk_ids  i32[T][k]   out: the k largest logits' expert ids, in descending logit order;
+ *                         equal logits go to the lower expert id; -0.0 equals +0.0
+ *   topk_w    f32[T][k]   out: gates = softmax over the k selected logits (sum to one)
+ * Errors: INVALID_ARG if T < 0, E < 1, E > 1024, k < 1, k > E or k > 64, or a null pointer. */
+moe_status moe_route(const float* logits, int32_t T, int32_t E, int32_t k,
+                     int32_t* topk_ids, float* topk_w, void* stream);
+
+/* moe_permute -- stable grouping of the R = T*k routed rows by expert.
+ *   topk_ids i32[T][k]    expert of row t*k+j (values in [0, E))
+ *   counts   i32[E]       out: rows routed to each expert
+ *   offsets  i32[E+1]     out: exclusive prefix sum of counts (offsets[E] = R)
+ *   perm     i32[R]       out: grouped row r holds routed row perm[r] = t*k+j, ordered by
+ *                         (expert, token, slot)
+ *   inv      i32[R]       out: inv[perm[r]] = r
+ *   ws       scratch of at least moe_permute_ws_bytes(T, k, E) bytes (may be NULL if that is 0)
+ * The result is deterministic (no order-dependent atomics).
+ * Errors: INVALID_ARG (bad sizes, null output, R >= 2^31), WORKSPACE (ws too small). */
+size_t moe_permute_ws_bytes(int32_t T, int32_t k, int32_t E);
+moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
+                       int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* moe_expert_ffn -- the routed experts ([Moet-README] release notes of -r23: FC1, SwiGLU,
+ * (MXFP8 quantisation for FP8 compute), FC2).  For grouped row r of expert e, with token
+ * t = perm[r] / k:
+ *     a = x[t] W1_e^T (fp32 accumulation), h = silu(a[:I]) * a[I:], y_perm[r] = h W2_e^T.
+ * Low-bit experts dequantise their codes inside the matmul kernels (bf16 operands, fp32
+ * accumulation, h rounded to bf16).  Hot MXFP4 experts are first converted to FP8 into slots
+ * of the workspace ([Day0-MXFP4] section 4), then computed with MXFP8 x and h on the FP8
+ * matrix cores.  Rows of experts with no tokens are not touched.
+ *   x        bf16 (u16 bits) [T][H]
+ *   counts, offsets, perm   as produced by moe_permute for the same topk_ids
+ *   y_perm   f32[R][H]   out (row r = grouped row r)
+ *   ws       workspace of at least moe_expert_ffn_ws_bytes(w, T, k, fp8_slots) bytes; the
+ *            number of FP8 slots used is the largest that fits, capped at n_hot, and the hot
+ *            experts are converted and computed in batches of that many.
+ * Requirements: H % 256 == 0, I % 256 == 0, H and I <= 16384; fmt W2 or W3.
+ * Errors: INVALID_ARG, UNSUPPORTED (format/shape not built), WORKSPACE. */
+size_t moe_expert_ffn_ws_bytes(const moe_weights* w, int32_t T, int32_t k, int32_t fp8_slots);
+moe_status moe_expert_ffn(const moe_weights* w, const uint16_t* x, int32_t T, int32_t k,
+                          const int32_t* counts, const int32_t* offsets, const int32_t* perm,
+                          float* y_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* moe_expert_ffn_stage -- run one stage of moe_expert_ffn.  Calling stages 0 .. n-1, with
+ * n = moe_expert_ffn_num_stages(w, T, k), in order on one stream with the same arguments and
+ * workspace is exactly moe_expert_ffn.  Each stage is a single kernel launch, so a caller can
+ * time the kernels one by one (HIP events on `stream`) or interleave other work between them.
+ * Stages of a low-bit layer: 0 = work list from offsets and x in MFMA operand order,
+ * 1 = FC1 + SwiGLU (h into the workspace), 2 = FC2 (y_perm).
+ * Errors: as moe_expert_ffn; INVALID_ARG for a stage out of range. */
+int32_t moe_expert_ffn_num_stages(const moe_weights* w, int32_t T, int32_t k);
+moe_status moe_expert_ffn_stage(const moe_weights* w, const uint16_t* x, int32_t T, int32_t k,
+                                const int32_t* counts, const int32_t* offsets, const int32_t* perm,
+                                float* y_perm, void* ws, size_t ws_bytes, int32_t stage,
+                                void* stream);
+
+/* moe_combine -- out[t] = sum over j = 0..k-1 (in that order) of topk_w[t][j] * y_perm[inv[t*k+j]],
+ * accumulated in fp32.  out is f32[T][H] if out_is_fp32, else bf16 (u16 bits, round to
+ * nearest even of the same fp32 sum).
+ * Errors: INVALID_ARG. */
+moe_status moe_combine(const float* y_perm, const int32_t* inv, const float* topk_w,
+                       int32_t T, int32_t k, int32_t H, void* out, int32_t out_is_fp32,
+                       void* stream);
+
+/* moe_mxfp4_to_fp8 -- [Day0-MXFP4] section 4: convert an MXFP4 matrix to FP8.  Each e2m1
+ * element becomes the e4m3fn byte of the same value (lossless, -0 -> 0x80); e8m0 scales are
+ * copied.  This is the conversion moe_expert_ffn runs on hot experts.
+ *   codes u8[rows][K/2], scales u8[rows][K/32] -> elems u8[rows][K], out_scales u8[rows][K/32]
+ * Errors: INVALID_ARG (K % 32 != 0, null pointer). */
+moe_status moe_mxfp4_to_fp8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int32_t K,
+                            uint8_t* elems, uint8_t* out_scales, void* stream);
+
+/* moe_mxfp8_quantize -- [OCP-MX] MXFP8 (e4m3fn) quantisation of bf16 rows, blocks of 32 along K:
+ * shared exponent floor(log2(amax)) - 8 (scale byte 0 for an all-zero block), elements
+ * round-to-nearest-even and saturate at +-448.  The quantisation moe_expert_ffn applies to
+ * the FC1 input of hot experts.
+ *   x bf16 [rows][K] -> elems u8[rows][K], scales u8[rows][K/32].   Errors: INVALID_ARG. */
+moe_status moe_mxfp8_quantize(const uint16_t* x, int64_t rows, int32_t K, uint8_t* elems,
+                              uint8_t* scales, void* stream);
+
+/* moe_debug_dequant -- decode one low-bit expert matrix with the same device code the FFN
+ * kernels use, into f32[rows][K] (W1: rows = 2I, K = H; W2: rows = H, K = I), in natural K
+ * order.  For tests: the decoded weights must equal the format definition bit for bit.
+ *   which: 1 (W1) or 2 (W2).   Errors: INVALID_ARG, UNSUPPORTED. */
+moe_status moe_debug_dequant(const moe_weights* w, int32_t e, int32_t which, float* out,
+                             void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* moe_status_str(moe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BITMOE_H */

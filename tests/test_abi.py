@@ -1,0 +1,85 @@
+"""The C ABI library loads and exports every function include/bitmoe.h declares (no GPU
+calls), and the host-side argument checks reject bad input without touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitmoe.h")
+LIB = os.path.join(ROOT, "bit_moe_expert_top_amd", "libbitmoe.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(moe_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine"):
+        assert n in names
+    assert len(names) >= 10
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.skip("libbitmoe.so not built")
+    return ctypes.CDLL(LIB)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    lib.moe_status_str.restype = ctypes.c_char_p
+    assert lib.moe_status_str(0) == b"MOE_OK"
+    assert lib.moe_status_str(-3) == b"MOE_ERR_WORKSPACE"
+
+
+def test_host_argument_checks_need_no_gpu(lib):
+    """Every check below fails on the host before anything is enqueued."""
+    p = ctypes.c_void_p(16)  # never dereferenced: the calls must reject the arguments first
+    lib.moe_route.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.moe_route(p, 4, 8, 0, p, p, None) == -1       # k < 1
+    assert lib.moe_route(p, 4, 8, 9, p, p, None) == -1       # k > E
+    assert lib.moe_route(p, 4, 2000, 2, p, p, None) == -1    # E too large
+    assert lib.moe_route(None, 4, 8, 2, p, p, None) == -1    # null input
+    assert lib.moe_route(None, 0, 8, 2, None, None, None) == 0  # T = 0 is a no-op
+    lib.moe_permute.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.moe_permute_ws_bytes.restype = ctypes.c_size_t
+    need = lib.moe_permute_ws_bytes(100000, 8, 384)
+    assert need > 0
+    assert lib.moe_permute(p, 100000, 8, 384, p, p, p, p, p, need - 1, None) == -3  # workspace
+    assert lib.moe_permute(p, 4, 8, 4, p, p, p, p, None, 0, None) == -1  # k > E
+    lib.moe_combine.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                                ctypes.c_void_p]
+    assert lib.moe_combine(p, p, p, 4, 2, 6, p, 1, None) == -1  # H % 4
+    assert lib.moe_combine(None, p, p, 4, 2, 8, p, 1, None) == -1
+
+
+def test_ffn_argument_checks(lib):
+    import sys
+    sys.path.insert(0, ROOT)
+    from bit_moe_expert_top_amd import _lib as L
+
+    p = 16
+    w = L.MoeWeights(8, 256, 512, L.MOE_FMT_W2, p, p, p, p, 0, None, None, None, None, None)
+    assert L.lib.moe_expert_ffn_ws_bytes(ctypes.byref(w), 16, 2, 0) > 0
+    bad = L.MoeWeights(8, 200, 512, L.MOE_FMT_W2, p, p, p, p, 0, None, None, None, None, None)
+    assert L.lib.moe_expert_ffn(ctypes.byref(bad), p, 16, 2, p, p, p, p, p, 1 << 30, None) == -1  # H % 256
+    assert L.lib.moe_expert_ffn(ctypes.byref(w), p, 16, 2, p, p, p, p, p, 10, None) == -3  # workspace
+    nofmt = L.MoeWeights(8, 256, 512, 7, p, p, p, p, 0, None, None, None, None, None)
+    assert L.lib.moe_expert_ffn(ctypes.byref(nofmt), p, 16, 2, p, p, p, p, p, 1 << 30, None) == -1
+    hot_missing = L.MoeWeights(8, 256, 512, L.MOE_FMT_W2, p, p, p, p, 2, None, None, None, None, None)
+    assert L.lib.moe_expert_ffn(ctypes.byref(hot_missing), p, 16, 2, p, p, p, p, p, 1 << 30, None) == -1
+    assert L.lib.moe_debug_dequant(ctypes.byref(w), 8, 1, p, None) == -1  # expert out of range

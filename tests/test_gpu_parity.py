@@ -1,0 +1,150 @@
+"""GPU parity: the HIP library (through the C ABI) against the fp64 CPU oracle on the same
+seeded inputs.  Routing ids, counts, offsets, perm, inv and decoded weights must match bit
+for bit; float outputs within max|gpu - oracle| <= tol * rms(oracle)."""
+import numpy as np
+import pytest
+import torch
+
+import moegen
+from oracle import formats as OF
+from oracle import moe as OM
+
+from _helpers import (TOL_BF16, bf16_bits_host, device_layer, host, layer_arrays, max_err_over_rms,
+                      oracle_layer, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from bit_moe_expert_top_amd import _lib
+
+    return _lib
+
+
+# ------------------------------------------------------------------ decoded weights
+@pytest.mark.parametrize("name,experts", [("tiny", [0, 5, 7]), ("decode", [0, 383])])
+def test_debug_dequant_bit_exact(L, name, experts):
+    sp, dw = device_layer(name)
+    lay = oracle_layer(name)
+    for e in experts:
+        for which in (1, 2):
+            got = host(L.moe_debug_dequant(dw, e, which)).astype(np.float64)
+            want = lay.dense(e, which)
+            assert np.array_equal(got, want), (name, e, which, np.argwhere(got != want)[:5])
+
+
+# ------------------------------------------------------------------ routing
+@pytest.mark.parametrize("T,E,k", [(16, 8, 2), (1, 384, 8), (64, 384, 8), (37, 512, 10), (5, 8, 8),
+                                   (300, 100, 7), (4096, 384, 8), (3, 1024, 64), (2, 64, 1)])
+def test_route_bit_exact_ids(L, T, E, k):
+    r = np.random.default_rng(T * 31 + E)
+    lg = r.standard_normal((T, E)).astype(np.float32)
+    lg[0, : E // 2] = 0.25          # ties
+    if T > 1:
+        lg[1, ::2] = -0.0
+        lg[1, 1::2] = 0.0
+    ids, gw = L.moe_route(to_dev(lg), k)
+    want_ids, want_g = OM.route(lg, k)
+    np.testing.assert_array_equal(host(ids), want_ids)
+    np.testing.assert_allclose(host(gw), want_g, rtol=2e-6, atol=1e-7)
+
+
+# ------------------------------------------------------------------ grouping
+@pytest.mark.parametrize("T,E,k", [(16, 8, 2), (1, 384, 8), (64, 384, 8), (37, 512, 10), (5, 8, 8),
+                                   (511, 384, 8), (513, 384, 8), (4096, 512, 10), (65536, 384, 8),
+                                   (1000, 1024, 3)])
+def test_permute_bit_exact(L, T, E, k):
+    r = np.random.default_rng(T + E + k)
+    lg = r.standard_normal((T, E)).astype(np.float32) - 1.1 * np.log(np.arange(1, E + 1))[None, :].astype(np.float32)
+    ids, _ = OM.route(lg, k)
+    counts, offsets, perm, inv = L.moe_permute(to_dev(ids), E)
+    wc, wo, wp, wi = OM.permute(ids, E)
+    np.testing.assert_array_equal(host(counts), wc)
+    np.testing.assert_array_equal(host(offsets), wo)
+    np.testing.assert_array_equal(host(perm), wp)
+    np.testing.assert_array_equal(host(inv), wi)
+
+
+def test_permute_empty_batch(L):
+    ids = torch.zeros((0, 2), dtype=torch.int32, device="cuda")
+    counts, offsets, perm, inv = L.moe_permute(ids, 8)
+    assert host(counts).tolist() == [0] * 8 and host(offsets).tolist() == [0] * 9
+
+
+# ------------------------------------------------------------------ combine
+def test_combine_bf16_is_rne_of_fp32(L):
+    r = np.random.default_rng(3)
+    T, k, H = 33, 4, 512
+    y = r.standard_normal((T * k, H)).astype(np.float32)
+    inv = r.permutation(T * k).astype(np.int32)
+    g = r.uniform(0, 1, (T, k)).astype(np.float32)
+    o32 = host(L.moe_combine(to_dev(y), to_dev(inv), to_dev(g), out_fp32=True))
+    o16 = host(L.moe_combine(to_dev(y), to_dev(inv), to_dev(g), out_fp32=False)).view(np.uint16)
+    want = OM.combine(y, inv, g, T, k)
+    assert max_err_over_rms(o32, want) < 1e-6
+    np.testing.assert_array_equal(o16, torch.from_numpy(o32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+
+
+# ------------------------------------------------------------------ the whole layer
+def _check_layer(L, name, T, sample_tokens=None, **override):
+    sp, dw = device_layer(name, **override)
+    lay = oracle_layer(name, **override)
+    b = moegen.batch(sp, T)
+    k = sp["k"]
+    res = L.layer_forward(dw, to_dev(b["logits"]), to_dev(b["x"]), k, out_fp32=True)
+    ids, gates = OM.route(b["logits"], k)
+    counts, offsets, perm, inv = OM.permute(ids, sp["E"])
+    np.testing.assert_array_equal(host(res["ids"]), ids)
+    np.testing.assert_array_equal(host(res["counts"]), counts)
+    np.testing.assert_array_equal(host(res["offsets"]), offsets)
+    np.testing.assert_array_equal(host(res["perm"]), perm)
+    np.testing.assert_array_equal(host(res["inv"]), inv)
+    toks = np.arange(T) if sample_tokens is None else np.asarray(sample_tokens)
+    experts = sorted(set(ids[toks].reshape(-1).tolist()))
+    y = OM.expert_ffn(lay, b["x"], k, offsets, perm, experts=experts)
+    out = OM.combine(np.nan_to_num(y), inv, gates, T, k)[toks]
+    got = host(res["out"])[toks]
+    err = max_err_over_rms(got, out)
+    print(f"{name} T={T}: max|err|/rms = {err:.4g}", flush=True)
+    assert err <= TOL_BF16
+    rows = np.concatenate([np.arange(offsets[e], offsets[e + 1]) for e in experts])
+    assert max_err_over_rms(host(res["y_perm"])[rows], y[rows]) <= TOL_BF16
+    # bf16 output is the RNE of the same fp32 sums
+    o16 = L.moe_combine(res["y_perm"], res["inv"], res["gates"], out_fp32=False)
+    ref16 = res["out"].to(torch.bfloat16).view(torch.int16)
+    assert torch.equal(o16, ref16)
+    return res
+
+
+@pytest.mark.parametrize("T", [16, 1, 5, 37, 64, 100])
+def test_layer_tiny(L, T):
+    _check_layer(L, "tiny", T)
+
+
+def test_layer_tiny_k1_and_kE(L):
+    _check_layer(L, "tiny", 9, k=1)
+    _check_layer(L, "tiny", 9, k=8)
+
+
+@pytest.mark.parametrize("T,sample", [(1, None), (8, None), (64, [0, 31, 63])])
+def test_layer_decode(L, T, sample):
+    _check_layer(L, "decode", T, sample)
+
+
+def test_layer_deterministic(L):
+    sp, dw = device_layer("tiny")
+    b = moegen.batch(sp, 64)
+    a = L.layer_forward(dw, to_dev(b["logits"]), to_dev(b["x"]), sp["k"])
+    c = L.layer_forward(dw, to_dev(b["logits"]), to_dev(b["x"]), sp["k"])
+    assert torch.equal(a["out"], c["out"]) and torch.equal(a["y_perm"], c["y_perm"])
+
+
+def test_empty_batch_is_a_noop(L):
+    sp, dw = device_layer("tiny")
+    x = torch.zeros((0, sp["H"]), dtype=torch.int16, device="cuda")
+    lg = torch.zeros((0, sp["E"]), dtype=torch.float32, device="cuda")
+    res = L.layer_forward(dw, lg, x, sp["k"])
+    assert res["out"].shape == (0, sp["H"])
