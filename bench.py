@@ -8,8 +8,9 @@ already resident in HBM.  Default workload: the decode layer (384 experts, top-8
 routing) at T = 64 tokens.
 
 Every step is timed with HIP events on the stream the kernels run on; the last-level
-caches are flushed between steps (outside the events) by writing a 1 GiB buffer, so the
-expert weights come from HBM.  The FC1 kernel (2/3 of the weight bytes) is the dominant
+caches are flushed between steps (outside the events) by *reading* a 1 GiB buffer, so the
+expert weights come from HBM.  (A write flush would leave the 256 MB last-level cache full of
+dirty lines whose write-back then competes with the timed kernels: a measurement artefact.)  The FC1 kernel (2/3 of the weight bytes) is the dominant
 kernel: its algorithmic bytes (packed weights of the experts that received tokens, x read
 once, h written once) divided by its event-timed duration give `roofline.achieved`.
 
@@ -70,33 +71,29 @@ def cpu_baseline(sp, batch, T, n_tok):
             "sample": f"first {n_tok} of the {T} tokens ({len(used)} experts), numpy fp64, {dt:.1f} s"}
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--layer", default="decode", help="decode | tiny")
-    ap.add_argument("--T", type=int, default=64)
-    ap.add_argument("--no-flush", action="store_true", help="do not flush caches between steps")
-    ap.add_argument("--cpu-tokens", type=int, default=4, help="tokens of the oracle's timed sample (0 = skip)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print("bench.py: this MoE layer path runs on one GPU; --gpus above 1 is not supported "
-              "(the multi-GPU split is described in DESIGN.md, not built)", file=sys.stderr)
-        sys.exit(2)
+def setup_layer(name: str):
+    import numpy as np  # noqa: F401
 
+    import moegen
+    from bit_moe_expert_top_amd import _lib as L
+
+    sp = moegen.spec(name)
+    print(f"[bench] generating layer {name} (E={sp['E']} k={sp['k']} H={sp['H']} I={sp['I']} {sp['fmt']})",
+          file=sys.stderr, flush=True)
+    arrays = moegen.weights(sp)
+    dw = L.DeviceWeights({"w2": 1, "w3": 2}[sp["fmt"]], sp["E"], sp["H"], sp["I"], arrays)
+    return sp, dw
+
+
+def measure(sp: dict, dw, T: int, steps: int, warmup: int, flush_between: bool = True) -> dict:
+    """Time `steps` layer steps on T tokens; returns the bench record (without cpu_baseline)."""
     import numpy as np
     import torch
 
     import moegen
     from bit_moe_expert_top_amd import _lib as L
 
-    sp = moegen.spec(args.layer)
-    T, k, E, H, I = args.T, sp["k"], sp["E"], sp["H"], sp["I"]
-    print(f"[bench] generating layer {args.layer} (E={E} k={k} H={H} I={I} {sp['fmt']}), T={T}",
-          file=sys.stderr, flush=True)
-    arrays = moegen.weights(sp)
-    dw = L.DeviceWeights({"w2": 1, "w3": 2}[sp["fmt"]], E, H, I, arrays)
+    k, E, H, I = sp["k"], sp["E"], sp["H"], sp["I"]
     batch = moegen.batch(sp, T)
     dev = torch.device("cuda")
     logits = torch.from_numpy(batch["logits"]).to(dev)
@@ -112,7 +109,7 @@ def main():
     y = torch.empty((R, H), dtype=torch.float32, device=dev)
     out = torch.empty((T, H), dtype=torch.int16, device=dev)
     n_stages = L.moe_expert_ffn_num_stages(dw, T, k)
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB, read to evict caches
     stream = torch.cuda.current_stream()
 
     def ev():
@@ -133,18 +130,18 @@ def main():
         if evs:
             evs[-1].record(stream)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     n_active = int((counts > 0).sum().item())
-    print(f"[bench] {n_active} experts active; timing {args.steps} steps", file=sys.stderr, flush=True)
+    print(f"[bench] T={T}: {n_active} experts active; timing {steps} steps", file=sys.stderr, flush=True)
 
-    all_evs = [[ev() for _ in range(2 + 2 * n_stages)] for _ in range(args.steps)]
+    all_evs = [[ev() for _ in range(2 + 2 * n_stages)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        if not args.no_flush:
-            flush.zero_()
+    for i in range(steps):
+        if flush_between:
+            flush.sum()
         step(all_evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -159,22 +156,21 @@ def main():
     fc1_bytes = w1b + T * H * 2 + R * I * 2
     fc1_gbs = fc1_bytes / (fc1_ms * 1e-3) / 1e9
     weight_gbs = (w1b + w2b) / ((fc1_ms + fc2_ms) * 1e-3) / 1e9
-
-    res = {
+    return {
         "metric": "MoE-layer tokens/sec (decode; weight HBM GB/s of the expert kernels in roofline)",
         "value": T / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; uniform 2-bit codes, bf16 group-32 scales, N(0,1) x, Zipf s=1.1 logits)",
-        "config": {"workload": f"{args.layer} MoE layer E={E} top-{k} H={H} I={I} {sp['fmt']} T={T}",
-                   "tokens": T, "experts_active": n_active, "cache_flush_between_steps": not args.no_flush},
+        "config": {"workload": f"{sp['name']} MoE layer E={E} top-{k} H={H} I={I} {sp['fmt']} T={T}",
+                   "tokens": T, "experts_active": n_active, "cache_flush_between_steps": flush_between},
         "roofline": {"bound": "hbm", "kernel": "FC1 + SwiGLU (w2_stream_kernel<1>)",
                      "achieved": fc1_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": fc1_gbs / HBM_PEAK_GBS, "traffic": None,
@@ -183,9 +179,29 @@ def main():
         "weight_GBps_fc1_fc2": weight_gbs,
         "wall_s_timed_loop_incl_flush": wall,
     }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layer", default="decode", help="decode | tiny")
+    ap.add_argument("--T", type=int, default=64)
+    ap.add_argument("--no-flush", action="store_true", help="do not flush caches between steps")
+    ap.add_argument("--cpu-tokens", type=int, default=4, help="tokens of the oracle's timed sample (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this MoE layer path runs on one GPU; --gpus above 1 is not supported "
+              "(the multi-GPU split is described in DESIGN.md, not built)", file=sys.stderr)
+        sys.exit(2)
+    sp, dw = setup_layer(args.layer)
+    res = measure(sp, dw, args.T, args.steps, args.warmup, not args.no_flush)
     if args.cpu_tokens > 0:
+        import moegen
+
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(sp, batch, T, min(args.cpu_tokens, T))
+        res["cpu_baseline"] = cpu_baseline(sp, moegen.batch(sp, args.T), args.T, min(args.cpu_tokens, args.T))
     print(json.dumps(res), flush=True)
 
 

@@ -18,12 +18,12 @@ inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 inline moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
-// Rows per work item of the streaming kernels, from the batch size alone (a group of one
-// expert never has more than T rows).  Larger groups are split into 64-row items.
-inline int stream_nt(int T) { return T <= 16 ? 1 : (T <= 32 ? 2 : 4); }
+// Rows per work item of the streaming kernels: a group of one expert is split into items
+// of at most 32 rows (two 16-token MFMA tiles).
+constexpr int kStreamChunk = 32;
 
 struct FfnLayout {
-  int nt, chunk;
+  int chunk;
   int64_t max_items;
   size_t plan_off, xp_off, h_off, total;
 };
@@ -31,16 +31,15 @@ struct FfnLayout {
 FfnLayout ffn_layout(const moe_weights* w, int T, int k) {
   FfnLayout L;
   const int64_t R = (int64_t)T * k;
-  L.nt = stream_nt(T);
-  L.chunk = 16 * L.nt;
+  L.chunk = kStreamChunk;
   L.max_items = (R + L.chunk - 1) / L.chunk + (R < w->E ? R : w->E);
   size_t off = 0;
   L.plan_off = off;
   off = align256(off + plan_bytes(L.max_items));
-  L.xp_off = off;
-  off = align256(off + (size_t)T * w->H * 2);
-  L.h_off = off;
-  off = align256(off + (size_t)R * w->I * 2);
+  L.xp_off = off;  // T rows + one zero row
+  off = align256(off + (size_t)(T + 1) * w->H * 2);
+  L.h_off = off;  // R rows + one zero row
+  off = align256(off + (size_t)(R + 1) * w->I * 2);
   L.total = off;
   return L;
 }
@@ -153,13 +152,14 @@ moe_status ffn_run_stage(const moe_weights* w, const uint16_t* x, int32_t T, int
   hipError_t e = hipSuccess;
   switch (stage) {
     case 0:
-      e = launch_prepare(offsets, w->E, L.chunk, w->hot_ids, w->n_hot, false, plan, x, T, w->H, xp, s);
+      e = launch_prepare(offsets, w->E, L.chunk, w->hot_ids, w->n_hot, false, plan, x, T, w->H, xp,
+                         xp + (size_t)T * w->H, w->H, hbuf + (size_t)T * k * w->I, w->I, s);
       break;
     case 1:
-      e = launch_lowbit_fc1(lw, w->E, w->H, w->I, k, xp, perm, plan, (int)L.max_items, L.nt, hbuf, s);
+      e = launch_lowbit_fc1(lw, w->E, w->H, w->I, k, xp, perm, plan, (int)L.max_items, T, hbuf, s);
       break;
     case 2:
-      e = launch_lowbit_fc2(lw, w->E, w->H, w->I, hbuf, plan, (int)L.max_items, L.nt, y_perm, s);
+      e = launch_lowbit_fc2(lw, w->E, w->H, w->I, k, hbuf, plan, (int)L.max_items, T, y_perm, s);
       break;
     default:
       return MOE_ERR_INVALID_ARG;

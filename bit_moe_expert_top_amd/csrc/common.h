@@ -36,6 +36,21 @@ __device__ __forceinline__ uint32_t byte_perm(uint32_t hi, uint32_t lo, uint32_t
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
+// Raw buffer loads: a uniform base + byte size (the "resource") and a per-lane 32-bit byte
+// offset.  A lane whose offset is >= the size reads zeros and makes no memory request, so
+// inactive lanes need no branch (the load stays unconditional).
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+constexpr uint32_t kOffNone = 0x80000000u;  // an offset past any buffer this library makes
+__device__ __forceinline__ buf_rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(buf_rsrc r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buf_load4(buf_rsrc r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+
 __device__ __forceinline__ int wave_lane() { return threadIdx.x & (kWave - 1); }
 
 template <typename T>

@@ -27,34 +27,32 @@ def v_perm_b32(s0: int, s1: int, sel: int) -> int:
     return out
 
 
-# --- 2-bit: the per-group byte table and the two pair extractions (ffn_lowbit.hip) ---
+# --- 2-bit: the per-group byte table and the decode of one word (ffn_lowbit.hip) ---
 def w2_table(s16):
     hb = (s16 >> 8) & 0xFF
-    lo = (((hb * 0x01010101) ^ 0x00008080) + 0x01000001) & 0xFFFFFFFF
-    hi = s16 & 0xFF
-    return lo, hi
+    lut = (((hb * 0x01010101) ^ 0x00008080) + 0x01000001) & 0xFFFFFFFF
+    return lut, s16 & 0xFF
 
 
-def w2_decode(w, half, lo, hi):
-    M, C = 0x03000300, 0x00040004
-    if half == 0:
-        sels = [((w >> (2 * m)) & M) | C for m in range(4)]
-    else:
-        sels = [(((w << (8 - 2 * m)) & 0xFFFFFFFF) & M) | C for m in range(4)]
-    return [v_perm_b32(hi, lo, s) for s in sels]
+def w2_decode_word(w, lut, lb):
+    """Eight dwords (two MFMA operands) from one word: for s = 0..3 the high bytes of codes
+    s, 4+s, 8+s, 12+s, then two interleaves with the scale's low byte."""
+    out = []
+    for s in range(4):
+        hb = v_perm_b32(0, lut, (w >> (2 * s)) & 0x03030303)
+        out += [v_perm_b32(lb, hb, 0x01040004), v_perm_b32(lb, hb, 0x03040204)]
+    return out  # dword 2s: (codes s, 4+s); dword 2s+1: (codes 8+s, 12+s)
 
 
 def emulate_w2_row(codes_row, scales_row):
     K = len(codes_row) * 16
     out = np.empty(K, dtype=np.uint16)
     for wc, w in enumerate(codes_row.tolist()):
-        lo, hi = w2_table(int(scales_row[wc // 2]))
-        p0, p1 = w2_decode(w, 0, lo, hi), w2_decode(w, 1, lo, hi)
-        for m in range(4):
-            out[16 * wc + 4 + m] = p0[m] & 0xFFFF
-            out[16 * wc + 12 + m] = p0[m] >> 16
-            out[16 * wc + m] = p1[m] & 0xFFFF
-            out[16 * wc + 8 + m] = p1[m] >> 16
+        lut, lb = w2_table(int(scales_row[wc // 2]))
+        d = w2_decode_word(w, lut, lb)
+        for s in range(4):
+            out[16 * wc + s], out[16 * wc + 4 + s] = d[2 * s] & 0xFFFF, d[2 * s] >> 16
+            out[16 * wc + 8 + s], out[16 * wc + 12 + s] = d[2 * s + 1] & 0xFFFF, d[2 * s + 1] >> 16
     return OF.bf16_value(out)
 
 
@@ -77,30 +75,30 @@ def test_w2_decode_trick_golden_words_and_scale_signs():
 
 
 # --- the k-slot order of the token operand (prepare kernel) and FC1's h store ---
-SLOT_K = [4, 12, 5, 13, 6, 14, 7, 15, 0, 8, 1, 9, 2, 10, 3, 11]
+# Within 16 consecutive k the MFMA slots hold k = 0,4,8,12, 1,5,9,13, 2,6,10,14, 3,7,11,15.
+SLOT_K = [4 * (p % 4) + p // 4 for p in range(16)]
 
 
 def kpos16(f):
     q, i = f >> 2, f & 3
-    return 2 * i + ((q & 1) ^ 1) * 8 + (q >> 1)
+    return 4 * i + q
 
 
 def test_slot_order_is_consistent():
+    assert SLOT_K == [0, 4, 8, 12, 1, 5, 9, 13, 2, 6, 10, 14, 3, 7, 11, 15]
     # FC1's store position of feature f is the slot that holds k = f
     assert [SLOT_K[kpos16(f)] for f in range(16)] == list(range(16))
-    # the decode pairs: dword m of half 0 holds (4+m, 12+m), of half 1 holds (m, 8+m)
-    pairs = [(4 + m, 12 + m) for m in range(4)] + [(m, 8 + m) for m in range(4)]
+    # the decode: operand 0 = dwords (0,4),(8,12),(1,5),(9,13); operand 1 = the same for s = 2, 3
+    pairs = [p for s in range(4) for p in ((s, 4 + s), (8 + s, 12 + s))]
     assert [k for p in pairs for k in p] == SLOT_K
 
 
 def test_prepare_x_byte_selectors():
     x = list(range(0x1000, 0x1010))  # 16 distinct bf16 bit patterns
     d = [x[2 * j] | (x[2 * j + 1] << 16) for j in range(8)]
-    a, b = d[:4], d[4:]
-    sel_lo, sel_hi = 0x05040100, 0x07060302
-    o = [v_perm_b32(b[2], a[2], sel_lo), v_perm_b32(b[2], a[2], sel_hi),
-         v_perm_b32(b[3], a[3], sel_lo), v_perm_b32(b[3], a[3], sel_hi),
-         v_perm_b32(b[0], a[0], sel_lo), v_perm_b32(b[0], a[0], sel_hi),
-         v_perm_b32(b[1], a[1], sel_lo), v_perm_b32(b[1], a[1], sel_hi)]
+    LO, HI = 0x05040100, 0x07060302
+    o = [v_perm_b32(d[2], d[0], LO), v_perm_b32(d[6], d[4], LO), v_perm_b32(d[2], d[0], HI),
+         v_perm_b32(d[6], d[4], HI), v_perm_b32(d[3], d[1], LO), v_perm_b32(d[7], d[5], LO),
+         v_perm_b32(d[3], d[1], HI), v_perm_b32(d[7], d[5], HI)]
     got = [v for dw in o for v in (dw & 0xFFFF, dw >> 16)]
     assert got == [x[k] for k in SLOT_K]
