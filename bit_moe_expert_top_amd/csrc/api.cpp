@@ -21,8 +21,11 @@ inline moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE
 // Rows per work item of the streaming kernels: a group of one expert is split into items
 // of at most 32 rows (two 16-token MFMA tiles).
 constexpr int kStreamChunk = 32;
+// Batches of at least this many tokens run the grouped-GEMM kernels (prefill shape).
+constexpr int kGemmMinTokens = 128;
 
 struct FfnLayout {
+  bool gemm;
   int chunk;
   int64_t max_items;
   size_t plan_off, xp_off, h_off, total;
@@ -31,15 +34,16 @@ struct FfnLayout {
 FfnLayout ffn_layout(const moe_weights* w, int T, int k) {
   FfnLayout L;
   const int64_t R = (int64_t)T * k;
-  L.chunk = kStreamChunk;
+  L.gemm = T >= kGemmMinTokens;
+  L.chunk = L.gemm ? kGemmRows : kStreamChunk;
   L.max_items = (R + L.chunk - 1) / L.chunk + (R < w->E ? R : w->E);
   size_t off = 0;
   L.plan_off = off;
   off = align256(off + plan_bytes(L.max_items));
-  L.xp_off = off;  // T rows + one zero row
-  off = align256(off + (size_t)(T + 1) * w->H * 2);
-  L.h_off = off;  // R rows + one zero row
-  off = align256(off + (size_t)(R + 1) * w->I * 2);
+  L.xp_off = off;  // x in k-slot order, T rows
+  off = align256(off + (size_t)T * w->H * 2);
+  L.h_off = off;  // h (bf16, k-slot order), R rows
+  off = align256(off + (size_t)R * w->I * 2);
   L.total = off;
   return L;
 }
@@ -152,14 +156,15 @@ moe_status ffn_run_stage(const moe_weights* w, const uint16_t* x, int32_t T, int
   hipError_t e = hipSuccess;
   switch (stage) {
     case 0:
-      e = launch_prepare(offsets, w->E, L.chunk, w->hot_ids, w->n_hot, false, plan, x, T, w->H, xp,
-                         xp + (size_t)T * w->H, w->H, hbuf + (size_t)T * k * w->I, w->I, s);
+      e = launch_prepare(offsets, w->E, L.chunk, w->hot_ids, w->n_hot, false, plan, x, T, w->H, xp, s);
       break;
     case 1:
-      e = launch_lowbit_fc1(lw, w->E, w->H, w->I, k, xp, perm, plan, (int)L.max_items, T, hbuf, s);
+      e = L.gemm ? launch_lowbit_gemm_fc1(lw, w->H, w->I, k, xp, perm, plan, (int)L.max_items, T, hbuf, s)
+                 : launch_lowbit_fc1(lw, w->E, w->H, w->I, k, xp, perm, plan, (int)L.max_items, T, hbuf, s);
       break;
     case 2:
-      e = launch_lowbit_fc2(lw, w->E, w->H, w->I, k, hbuf, plan, (int)L.max_items, T, y_perm, s);
+      e = L.gemm ? launch_lowbit_gemm_fc2(lw, w->H, w->I, k, hbuf, plan, (int)L.max_items, T, y_perm, s)
+                 : launch_lowbit_fc2(lw, w->E, w->H, w->I, k, hbuf, plan, (int)L.max_items, T, y_perm, s);
       break;
     default:
       return MOE_ERR_INVALID_ARG;

@@ -68,9 +68,7 @@ __global__ __launch_bounds__(1024) void prepare_kernel(const int32_t* __restrict
                                                        int n_hot, int want_hot,
                                                        int32_t* __restrict__ plan,
                                                        const uint4* __restrict__ x, int nchunks,
-                                                       uint4* __restrict__ xp, uint4* __restrict__ zero_a,
-                                                       int zero_a_n, uint4* __restrict__ zero_b,
-                                                       int zero_b_n) {
+                                                       uint4* __restrict__ xp) {
   if (blockIdx.x > 0) {
     const int c = (blockIdx.x - 1) * 1024 + threadIdx.x;
     if (c >= nchunks) return;
@@ -89,9 +87,7 @@ __global__ __launch_bounds__(1024) void prepare_kernel(const int32_t* __restrict
     xp[2 * c + 1] = o1;
     return;
   }
-  // block 0: zero rows read by lanes past an item's tokens, then the work list
-  for (int i = threadIdx.x; i < zero_a_n; i += 1024) zero_a[i] = make_uint4(0u, 0u, 0u, 0u);
-  for (int i = threadIdx.x; i < zero_b_n; i += 1024) zero_b[i] = make_uint4(0u, 0u, 0u, 0u);
+  // block 0: the work list
   __shared__ int scan_tmp[1024 / kWave + 1];
   __shared__ int16_t slot_of[1024];
   for (int e = threadIdx.x; e < E; e += 1024) slot_of[e] = -1;
@@ -120,14 +116,11 @@ __global__ __launch_bounds__(1024) void prepare_kernel(const int32_t* __restrict
 
 hipError_t launch_prepare(const int32_t* offsets, int E, int chunk_rows, const int32_t* hot_ids,
                           int n_hot, bool want_hot, int32_t* plan, const uint16_t* x, int T, int H,
-                          uint16_t* xp, uint16_t* zero_a, int zero_a_elems, uint16_t* zero_b,
-                          int zero_b_elems, hipStream_t s) {
+                          uint16_t* xp, hipStream_t s) {
   const int nchunks = xp ? T * (H / 16) : 0;
   const int blocks = 1 + (nchunks + 1023) / 1024;
   prepare_kernel<<<blocks, 1024, 0, s>>>(offsets, E, chunk_rows, hot_ids, n_hot, want_hot ? 1 : 0,
-                                         plan, (const uint4*)x, nchunks, (uint4*)xp,
-                                         (uint4*)zero_a, zero_a_elems / 8, (uint4*)zero_b,
-                                         zero_b_elems / 8);
+                                         plan, (const uint4*)x, nchunks, (uint4*)xp);
   return hipGetLastError();
 }
 

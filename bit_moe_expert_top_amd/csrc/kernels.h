@@ -36,21 +36,27 @@ struct LowbitWeights {
 //   int32 header[4]: [0] = number of chunks; then int4 items {expert, first row, rows, 0}.
 size_t plan_bytes(int64_t max_items);
 // One launch: the work list, and (if xp) x stored in the k-slot order of the MFMA operand.
-// zero_a / zero_b: bf16 rows (elems a multiple of 8, 16-byte aligned) set to zero: the rows
-// that lanes past an item's tokens read in the streaming kernels.
 hipError_t launch_prepare(const int32_t* offsets, int E, int chunk_rows, const int32_t* hot_ids,
                           int n_hot, bool want_hot, int32_t* plan, const uint16_t* x, int T, int H,
-                          uint16_t* xp, uint16_t* zero_a, int zero_a_elems, uint16_t* zero_b,
-                          int zero_b_elems, hipStream_t s);
+                          uint16_t* xp, hipStream_t s);
 
-// Decode-style kernels: weight-streaming, MFMA on 16-token tiles.  xp has T+1 rows and hbuf
-// T*k+1 rows; the last row of each is the zero row.
+// Decode-style kernels: weight-streaming, MFMA on 16-token tiles.
 hipError_t launch_lowbit_fc1(const LowbitWeights& w, int E, int H, int I, int k,
                              const uint16_t* xp, const int32_t* perm, const int32_t* plan,
                              int max_items, int T, uint16_t* hbuf, hipStream_t s);
 hipError_t launch_lowbit_fc2(const LowbitWeights& w, int E, int H, int I, int k,
                              const uint16_t* hbuf, const int32_t* plan, int max_items, int T,
                              float* y, hipStream_t s);
+
+// Prefill-sized groups: grouped GEMM on MFMA 32x32x16 with the codes decoded into LDS tiles.
+// Work items of at most kGemmRows rows.
+constexpr int kGemmRows = 128;
+hipError_t launch_lowbit_gemm_fc1(const LowbitWeights& w, int H, int I, int k, const uint16_t* xp,
+                                  const int32_t* perm, const int32_t* plan, int max_items, int T,
+                                  uint16_t* hbuf, hipStream_t s);
+hipError_t launch_lowbit_gemm_fc2(const LowbitWeights& w, int H, int I, int k,
+                                  const uint16_t* hbuf, const int32_t* plan, int max_items, int T,
+                                  float* y, hipStream_t s);
 
 hipError_t launch_debug_dequant(const LowbitWeights& w, int E, int H, int I, int e, int which,
                                 float* out, hipStream_t s);

@@ -119,7 +119,7 @@ def _check_layer(L, name, T, sample_tokens=None, **override):
     return res
 
 
-@pytest.mark.parametrize("T", [16, 1, 5, 37, 64, 100])
+@pytest.mark.parametrize("T", [16, 1, 5, 37, 64, 100, 128, 300, 1000])
 def test_layer_tiny(L, T):
     _check_layer(L, "tiny", T)
 
@@ -132,6 +132,16 @@ def test_layer_tiny_k1_and_kE(L):
 @pytest.mark.parametrize("T,sample", [(1, None), (8, None), (64, [0, 31, 63])])
 def test_layer_decode(L, T, sample):
     _check_layer(L, "decode", T, sample)
+
+
+@pytest.mark.parametrize("T,sample", [(256, [0, 100, 255])])
+def test_layer_decode_shape_gemm_path(L, T, sample):
+    _check_layer(L, "decode", T, sample)
+
+
+@pytest.mark.parametrize("T,sample", [(8192, [0, 4097, 8191])])
+def test_layer_prefill(L, T, sample):
+    _check_layer(L, "prefill", T, sample)
 
 
 def test_layer_deterministic(L):
