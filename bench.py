@@ -27,7 +27,43 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+GEMM_MIN_TOKENS = 128          # the library runs the grouped-GEMM kernels from this batch size
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+METRIC = "MoE-layer tokens/sec + weight HBM GB/s (decode) / MFMA % (prefill)"
+CSRC = os.path.join(ROOT, "bit_moe_expert_top_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def csrc_digest() -> str:
+    """sha256 over the kernel sources: a measured HBM-traffic figure is valid only for these."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel, from a committed counter summary under
+    profiles/ (a line `bench-traffic: {json}`), if it was taken on the current sources."""
+    if not os.path.isdir(PROFILES):
+        return None
+    digest = csrc_digest()
+    for name in sorted(os.listdir(PROFILES)):
+        if not name.endswith(".md"):
+            continue
+        with open(os.path.join(PROFILES, name)) as f:
+            for line in f:
+                if line.startswith("bench-traffic:"):
+                    rec = json.loads(line[len("bench-traffic:"):])
+                    if rec.get("workload") == workload and rec.get("csrc_sha256") == digest:
+                        return rec["bytes_per_launch"]
+    return None
 
 
 def weight_bytes_per_expert(sp: dict, which: int) -> int:
@@ -153,11 +189,28 @@ def measure(sp: dict, dw, T: int, steps: int, warmup: int, flush_between: bool =
     fc2_ms = float(np.mean(stage_ms[2]))
     w1b = n_active * weight_bytes_per_expert(sp, 1)
     w2b = n_active * weight_bytes_per_expert(sp, 2)
-    fc1_bytes = w1b + T * H * 2 + R * I * 2
-    fc1_gbs = fc1_bytes / (fc1_ms * 1e-3) / 1e9
-    weight_gbs = (w1b + w2b) / ((fc1_ms + fc2_ms) * 1e-3) / 1e9
+    gemm = T >= GEMM_MIN_TOKENS
+    workload = f"{sp['name']} MoE layer E={E} top-{k} H={H} I={I} {sp['fmt']} T={T}"
+    if gemm:
+        # prefill-sized: FC1 is a grouped GEMM; algorithmic flops = 2 * R * (2I) * H
+        fc1_flops = 2.0 * R * (2 * I) * H
+        achieved = fc1_flops / (fc1_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": "moe_expert_ffn stage 1: FC1 + SwiGLU grouped GEMM (w2_gemm_kernel<1>)",
+                "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / BF16_PEAK_TFLOPS, "alg_flops_per_launch": fc1_flops}
+    else:
+        # decode-sized: FC1 streams the packed W1 bytes of every expert that received a
+        # token, reads x once and writes h once
+        fc1_bytes = w1b + T * H * 2 + R * I * 2
+        achieved = fc1_bytes / (fc1_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "moe_expert_ffn stage 1: FC1 + SwiGLU weight streaming (w2_stream_kernel<1, G>)",
+                "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "alg_bytes_per_launch": fc1_bytes}
+    roof["traffic"] = measured_traffic(workload)
+    roof["avg_launch_ms"] = fc1_ms
+    all_flops = 2.0 * R * 3 * I * H
     return {
-        "metric": "MoE-layer tokens/sec (decode; weight HBM GB/s of the expert kernels in roofline)",
+        "metric": METRIC,
         "value": T / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -168,17 +221,32 @@ def measure(sp: dict, dw, T: int, steps: int, warmup: int, flush_between: bool =
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded; uniform 2-bit codes, bf16 group-32 scales, N(0,1) x, Zipf s=1.1 logits)",
-        "config": {"workload": f"{sp['name']} MoE layer E={E} top-{k} H={H} I={I} {sp['fmt']} T={T}",
-                   "tokens": T, "experts_active": n_active, "cache_flush_between_steps": flush_between},
-        "roofline": {"bound": "hbm", "kernel": "FC1 + SwiGLU (w2_stream_kernel<1>)",
-                     "achieved": fc1_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": fc1_gbs / HBM_PEAK_GBS, "traffic": None,
-                     "alg_bytes_per_launch": fc1_bytes, "avg_launch_ms": fc1_ms},
+        "data": f"synthetic (seeded; uniform {sp['fmt']} codes and scales, N(0,1) bf16 x, Zipf s=1.1 router logits)",
+        "config": {"workload": workload, "tokens": T, "experts_active": n_active,
+                   "cache_flush_between_steps": flush_between},
+        "roofline": roof,
         "stages_ms": {"route+permute+prepare+combine": ms - fc1_ms - fc2_ms, "fc1": fc1_ms, "fc2": fc2_ms},
-        "weight_GBps_fc1_fc2": weight_gbs,
+        "weight_GBps_fc1_fc2": (w1b + w2b) / ((fc1_ms + fc2_ms) * 1e-3) / 1e9,
+        "ffn_TFLOPs_fc1_fc2": all_flops / ((fc1_ms + fc2_ms) * 1e-3) / 1e12,
+        "ms_per_step_min": float(np.min(step_ms)),
+        "ms_per_step_median": float(np.median(step_ms)),
         "wall_s_timed_loop_incl_flush": wall,
     }
+
+
+def copy_calibration(mib: int):
+    """A plain device copy of known size (mib MiB read, mib MiB written), run after the timed
+    region so that one counter run sees both it and the timed kernels: FETCH_SIZE and
+    WRITE_SIZE of this copy scale the same counters of the other kernels to bytes."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[bench] copy calibration: {mib} MiB read + {mib} MiB written", file=sys.stderr, flush=True)
 
 
 def main():
@@ -189,7 +257,9 @@ def main():
     ap.add_argument("--layer", default="decode", help="decode | tiny")
     ap.add_argument("--T", type=int, default=64)
     ap.add_argument("--no-flush", action="store_true", help="do not flush caches between steps")
-    ap.add_argument("--cpu-tokens", type=int, default=4, help="tokens of the oracle's timed sample (0 = skip)")
+    ap.add_argument("--cpu-tokens", type=int, default=8, help="tokens of the oracle's timed sample (0 = skip)")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="after timing, run a plain copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this MoE layer path runs on one GPU; --gpus above 1 is not supported "
@@ -197,6 +267,8 @@ def main():
         sys.exit(2)
     sp, dw = setup_layer(args.layer)
     res = measure(sp, dw, args.T, args.steps, args.warmup, not args.no_flush)
+    if args.copy_calib_mib > 0:
+        copy_calibration(args.copy_calib_mib)
     if args.cpu_tokens > 0:
         import moegen
 

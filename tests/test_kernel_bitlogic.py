@@ -102,3 +102,110 @@ def test_prepare_x_byte_selectors():
          v_perm_b32(d[3], d[1], HI), v_perm_b32(d[7], d[5], HI)]
     got = [v for dw in o for v in (dw & 0xFFFF, dw >> 16)]
     assert got == [x[k] for k in SLOT_K]
+
+
+# --- 3-bit: the per-group byte tables and the decode of one 96-bit field (ffn_w3.hip) ---
+# A group's table holds the bf16 bytes of LEVEL[c] * e4m3(s) / 64 for c = 0..7: LB0/HB0 the
+# low/high bytes of c = 0..3 (levels -8,-5,-3,-1), LB1/HB1 those of c = 4..7 (1,3,5,8).
+def e4m3_over_64_f32_bits(b):
+    """fp32 bits of e4m3fn(b) / 64 by the kernels' integer path (finite bytes)."""
+    mag = b & 0x7F
+    if mag >> 3:
+        bits = (mag << 20) + (114 << 23)
+    else:
+        bits = int(np.float32(mag).view(np.uint32)) if mag == 0 else \
+            int((np.float32(mag) * np.float32(2.0 ** -15)).view(np.uint32))
+    return bits | ((b & 0x80) << 24)
+
+
+def f32_bits_mul(bits, m):
+    return int((np.uint32(bits).view(np.float32) * np.float32(m)).view(np.uint32))
+
+
+def w3_table(b):
+    f1 = e4m3_over_64_f32_bits(b)
+    f3, f5, f8 = f32_bits_mul(f1, 3), f32_bits_mul(f1, 5), f32_bits_mul(f1, 8)
+    p13 = v_perm_b32(f3, f1, 0x07030602)   # [lo1, lo3, hi1, hi3]
+    p58 = v_perm_b32(f8, f5, 0x07030602)   # [lo5, lo8, hi5, hi8]
+    lb1 = v_perm_b32(p58, p13, 0x05040100)
+    hb1 = v_perm_b32(p58, p13, 0x07060302)
+    lb0 = v_perm_b32(0, lb1, 0x00010203)
+    hb0 = v_perm_b32(0, hb1, 0x00010203) ^ 0x80808080
+    return hb1, hb0, lb1, lb0
+
+
+def pk_lshr16(v, a, b):
+    lo, hi = v & 0xFFFF, v >> 16
+    return (lo >> a) | ((hi >> b) << 16)
+
+
+def alignbit(hi, lo, s):
+    return (((hi << 32) | lo) >> s) & 0xFFFFFFFF
+
+
+def w3_lookup(sel, tab):
+    hb1, hb0, lb1, lb0 = tab
+    hb = v_perm_b32(hb1, hb0, sel)
+    lb = v_perm_b32(lb1, lb0, sel)
+    return [v_perm_b32(hb, lb, 0x05010400), v_perm_b32(hb, lb, 0x07030602)]
+
+
+M7 = 0x07070707
+
+
+def w3_decode_field(w0, w1, w2, tab):
+    """Four MFMA operands (16 dwords) from the three words of one 32-code field."""
+    z = v_perm_b32(w2, w0, 0x04020500)        # [B0, B9, B2, B8]
+    x = v_perm_b32(w1, w0, 0x04010603)        # [B3, B6, B1, B4]
+    y = v_perm_b32(w2, w1, 0x07010603)        # [B7, B10, B5, B11]
+    s0, s1, s2 = alignbit(w1, w0, 2), alignbit(w2, w1, 2), w2 >> 2
+    u = v_perm_b32(s1, s0, 0x04010300)        # stream>>2 bytes [S0, S3, S1, S4]
+    v = v_perm_b32(s2, s1, 0x06030502)        # [S6, S9, S7, S10]
+    sels = [pk_lshr16(z, 0, 2) & M7, pk_lshr16(z, 3, 5) & M7,
+            pk_lshr16(x, 0, 1) & M7, pk_lshr16(x, 3, 4) & M7,
+            pk_lshr16(y, 1, 2) & M7, pk_lshr16(y, 4, 5) & M7,
+            pk_lshr16(u, 4, 5) & M7, pk_lshr16(v, 4, 5) & M7]
+    return [d for s in sels for d in w3_lookup(s, tab)]
+
+
+# code index held by each of the 32 slots of a field (operand o = slots 8o .. 8o+7)
+SLOT3 = [0, 24, 6, 22, 1, 25, 7, 23, 8, 16, 3, 11, 9, 17, 4, 12,
+         19, 27, 14, 30, 20, 28, 15, 31, 2, 10, 5, 13, 18, 26, 21, 29]
+
+
+def emulate_w3_row(codes_row, scales_row):
+    K = len(codes_row) // 3 * 32
+    out = np.empty(K, dtype=np.uint16)
+    for f in range(K // 32):
+        tab = w3_table(int(scales_row[f // 2]))
+        d = w3_decode_field(*[int(c) for c in codes_row[3 * f:3 * f + 3]], tab)
+        halves = [h for dw in d for h in (dw & 0xFFFF, dw >> 16)]
+        for slot, c in enumerate(SLOT3):
+            out[32 * f + c] = halves[slot]
+    return OF.bf16_value(out)
+
+
+def test_slot3_is_a_permutation():
+    assert sorted(SLOT3) == list(range(32))
+
+
+def test_w3_decode_trick_matches_oracle():
+    sp = moegen.spec("w3")
+    ex = moegen.expert(sp, 5)
+    want = OF.dequant_w3(ex["w1_codes"][:4, :48], ex["w1_scales"][:4, :8])
+    for r in range(4):
+        got = emulate_w3_row(ex["w1_codes"][r, :48], ex["w1_scales"][r, :8])
+        np.testing.assert_array_equal(got, want[r])
+
+
+def test_w3_decode_every_finite_scale_byte_and_golden_fields():
+    fields = [(0x88FAC688, 0xC688FAC6, 0xFAC688FA), (0x77053977, 0x39770539, 0x05397705),
+              (0, 0, 0), (0xFFFFFFFF, 0xFFFFFFFF, 0xFFFFFFFF), (0x9C3A71E5, 0x0F1E2D3C, 0xA5A55A5A)]
+    for b in range(256):
+        if b & 0x7F == 0x7F:
+            continue  # NaN encodings are not valid scales
+        for f in fields:
+            codes = np.array(f + f, np.uint32)
+            got = emulate_w3_row(codes, np.array([b], np.uint8))
+            want = OF.dequant_w3(codes[None, :], np.array([[b]], np.uint8))[0]
+            np.testing.assert_array_equal(got, want, err_msg=f"scale byte {b:#x}")
