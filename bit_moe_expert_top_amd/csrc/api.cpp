@@ -137,7 +137,7 @@ moe_status ffn_check(const moe_weights* w, const uint16_t* x, int32_t T, int32_t
   if ((int64_t)T * k >= ((int64_t)1 << 31)) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!x || !counts || !offsets || !perm || !y_perm) return MOE_ERR_INVALID_ARG;
-  if (w->fmt != MOE_FMT_W2 || w->n_hot != 0) return MOE_ERR_UNSUPPORTED;
+  if (w->n_hot != 0) return MOE_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < ffn_layout(w, T, k).total) return MOE_ERR_WORKSPACE;
   return MOE_OK;
 }
@@ -156,7 +156,7 @@ moe_status ffn_run_stage(const moe_weights* w, const uint16_t* x, int32_t T, int
   hipError_t e = hipSuccess;
   switch (stage) {
     case 0:
-      e = launch_prepare(offsets, w->E, L.chunk, w->hot_ids, w->n_hot, false, plan, x, T, w->H, xp, s);
+      e = launch_prepare(offsets, w->E, L.chunk, w->hot_ids, w->n_hot, false, plan, x, T, w->H, lw.fmt, xp, s);
       break;
     case 1:
       e = L.gemm ? launch_lowbit_gemm_fc1(lw, w->H, w->I, k, xp, perm, plan, (int)L.max_items, T, hbuf, s)
@@ -226,7 +226,6 @@ moe_status moe_debug_dequant(const moe_weights* w, int32_t e, int32_t which, flo
   moe_status st = check_weights(w);
   if (st != MOE_OK) return st;
   if (e < 0 || e >= w->E || (which != 1 && which != 2) || !out) return MOE_ERR_INVALID_ARG;
-  if (w->fmt != MOE_FMT_W2) return MOE_ERR_UNSUPPORTED;
   return from_hip(launch_debug_dequant(lowbit(w), w->E, w->H, w->I, e, which, out,
                                        as_stream(stream)));
 }

@@ -1,25 +1,25 @@
-// Expert FFN for prefill-sized groups: a grouped GEMM on the matrix cores with the 2-bit
+// Expert FFN for prefill-sized groups: a grouped GEMM on the matrix cores with the low-bit
 // codebook weights decoded into bf16 tiles in LDS.
 //
 // [Moet-README] release notes of -r23: the prefill MoE is FC1 + SwiGLU, then FC2, over the
-// routed rows of each expert.  [Moet-QA] (2-bit experts): codes on {-4,-1,1,4}, one bf16
-// scale per 32 weights along K.
+// routed rows of each expert.  [Moet-QA]: 2-bit codes on {-4,-1,1,4}, a bf16 scale per 32
+// along K.  [Strata-R9700] path 6: 3-bit codes on eight levels, an e4m3 scale / 64 per 64.
 //
 // Work item = (row tile of <= 128 grouped rows of one expert, column tile of 128 weight rows).
 // A workgroup of 4 waves (2 x 2) computes the 128 x 128 tile with v_mfma_f32_32x32x16_bf16,
 // each wave 64 x 64 (2 x 2 MFMA tiles).  Per 64-wide K step the workgroup loads the token rows
-// (16 KB, gathered) and the packed codes of its 128 weight rows (2 KB + 512 B of scales),
-// decodes the codes to bf16 into LDS (the same byte-table decode as the streaming kernels),
-// and runs 16 MFMAs per wave; LDS is double buffered so the next step's loads overlap.
-// Token operand and decoded weights share the k-slot order of the streaming path (a 4 x 4
-// transpose inside every 16 k): x comes permuted from the prepare kernel and FC1 writes h
-// permuted, so A and B always agree.
+// (16 KB, gathered) and the packed codes of its 128 weight rows, decodes the codes to exact
+// bf16 into LDS (the same decode as the streaming kernels, lowbit_fmt.h), and runs 16 MFMAs
+// per wave; LDS is double buffered so the next step's loads overlap.  Token operand and
+// decoded weights share the format's k-slot order: x comes permuted from the prepare kernel
+// and FC1 writes h permuted, so A and B always agree.
 //   FC1 column tile n: wave column wn holds gate rows 64n + 32wn + [0,32) and the up rows
 //       I + 64n + 32wn + [0,32) as its two MFMA column tiles, so gate and up of one h column
 //       sit in the same lane and SwiGLU is applied in the epilogue (h stored bf16).
 //   FC2 column tile n: weight rows 128n + [0,128); the epilogue stores y (fp32).
 #include "common.h"
 #include "kernels.h"
+#include "lowbit_fmt.h"
 
 namespace bitmoe {
 
@@ -33,34 +33,14 @@ __device__ __forceinline__ f32x16 mfma_32x32x16_bf16(u32x4 a, u32x4 b, f32x16 c)
                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// 2-bit group table and decode (identical bit logic to the streaming kernels).
-__device__ __forceinline__ void g2_table(uint32_t s16, uint32_t& lut, uint32_t& lb) {
-  const uint32_t hb = (s16 >> 8) & 0xFFu;
-  lut = ((hb * 0x01010101u) ^ 0x00008080u) + 0x01000001u;
-  lb = s16 & 0xFFu;
-}
-template <int HALF>
-__device__ __forceinline__ u32x4 g2_decode(uint32_t w, uint32_t lut, uint32_t lb) {
-  u32x4 r;
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int sh = 2 * (2 * HALF + u);
-    const uint32_t hb = byte_perm(0u, lut, (w >> sh) & 0x03030303u);
-    r[2 * u] = byte_perm(lb, hb, 0x01040004u);
-    r[2 * u + 1] = byte_perm(lb, hb, 0x03040204u);
-  }
-  return r;
-}
-__device__ __forceinline__ int g_kpos16(int f) { return 4 * (f & 3) + (f >> 2); }
-
 constexpr int kBM = 128, kBN = 128, kBK = 64;
 constexpr int kLdsRow = kBK + 8;                  // bf16 per LDS row (16 B of padding)
 constexpr int kTileElems = kBM * kLdsRow;         // one operand tile
 constexpr int kGemmLds = 2 * 2 * kTileElems * 2;  // 2 buffers x (A + B) x bf16 = 73,728 B
 
-template <int FC>
-__global__ __launch_bounds__(256, 2) void w2_gemm_kernel(
-    const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales, int rows_per_expert,
+template <class F, int FC>
+__global__ __launch_bounds__(256, 2) void gemm_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int rows_per_expert,
     int K, int width, int ktop, const uint16_t* __restrict__ asrc, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ plan, uint32_t asrc_bytes, void* __restrict__ out) {
   extern __shared__ __align__(16) uint16_t lds[];
@@ -70,7 +50,8 @@ __global__ __launch_bounds__(256, 2) void w2_gemm_kernel(
   const int4* items = reinterpret_cast<const int4*>(plan + 4);
   const int n_ntiles = FC == 1 ? width / 64 : rows_per_expert / kBN;
   const int total = n_items * n_ntiles;
-  const int wpr = K / 16, spr = K / 32, nk = K / kBK;
+  const uint32_t cbr = F::code_bytes((uint32_t)K), sbr = F::scale_bytes((uint32_t)K);
+  const int nk = K / kBK;
 
   for (int task = blockIdx.x; task < total; task += gridDim.x) {
     const int item = task / n_ntiles, nt_i = task - item * n_ntiles;
@@ -94,7 +75,7 @@ __global__ __launch_bounds__(256, 2) void w2_gemm_kernel(
         aoff[u] = (tok * (uint32_t)K + 8u * (tid & 7)) * 2u;
       }
     }
-    // B: weight row j = tid >> 1 of the tile, half h = tid & 1 of its 64 codes (2 words).
+    // B: weight row j = tid >> 1 of the tile, half h = tid & 1 of its 64 codes (32 codes).
     const int j = tid >> 1, hsel = tid & 1;
     int wrow;
     if (FC == 1) {
@@ -103,21 +84,29 @@ __global__ __launch_bounds__(256, 2) void w2_gemm_kernel(
     } else {
       wrow = kBN * nt_i + j;
     }
-    const buf_rsrc rc = make_rsrc(codes + ebase * wpr, (uint32_t)(rows_per_expert * wpr * 4));
-    const buf_rsrc rs = make_rsrc(scales + ebase * spr, (uint32_t)(rows_per_expert * spr * 2));
-    const uint32_t coff = (uint32_t)(wrow * wpr * 4) + 8u * hsel;
-    const uint32_t soff = (uint32_t)(wrow * spr * 2) + 2u * hsel;
+    const buf_rsrc rc = make_rsrc(codes + ebase * cbr, (uint32_t)rows_per_expert * cbr);
+    const buf_rsrc rs = make_rsrc(scales + ebase * sbr, (uint32_t)rows_per_expert * sbr);
+    const uint32_t coff = (uint32_t)wrow * cbr + F::code_bytes(32u * hsel);
+    // 2-bit: the half's own bf16 scale; 3-bit: the step's one scale byte (shared by both halves)
+    const uint32_t soff = (uint32_t)wrow * sbr + (F::kId == W2Fmt::kId ? 2u * hsel : 0u);
+    const uint32_t cstep = F::code_bytes(kBK), sstep = F::scale_bytes(kBK);
 
     // register staging of one K step
     u32x4 areg[4];
-    uint64_t creg;
+    uint32_t creg[F::kFieldWords];
     uint32_t sreg;
     auto load_step = [&](int kb) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) areg[u] = buf_load16(ra, aoff[u] + (uint32_t)kb * kBK * 2u);
-      creg = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(
-                                              rc, (int)(coff + (uint32_t)kb * 16u), 0, 0));
-      sreg = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, (int)(soff + (uint32_t)kb * 4u), 0, 0);
+      const uint32_t co = coff + (uint32_t)kb * cstep, so = soff + (uint32_t)kb * sstep;
+      const uint64_t c01 = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rc, (int)co, 0, 0));
+      creg[0] = (uint32_t)c01;
+      creg[1] = (uint32_t)(c01 >> 32);
+      if constexpr (F::kFieldWords == 3) creg[2] = buf_load4(rc, co + 8u);
+      if constexpr (F::kId == W2Fmt::kId)
+        sreg = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, (int)so, 0, 0);
+      else
+        sreg = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, (int)so, 0, 0);
     };
     auto store_step = [&](int buf) {
       uint16_t* la = lds + buf * 2 * kTileElems;
@@ -127,14 +116,10 @@ __global__ __launch_bounds__(256, 2) void w2_gemm_kernel(
         const int r = (tid >> 3) + 32 * u;
         *reinterpret_cast<u32x4*>(la + r * kLdsRow + 8 * (tid & 7)) = areg[u];
       }
-      uint32_t lut, lb;
-      g2_table(sreg & 0xFFFFu, lut, lb);
+      const typename F::Tab tab = F::table32(sreg);
       uint16_t* dst = lbm + j * kLdsRow + 32 * hsel;
-      const uint32_t w0 = (uint32_t)creg, w1 = (uint32_t)(creg >> 32);
-      *reinterpret_cast<u32x4*>(dst + 0) = g2_decode<0>(w0, lut, lb);
-      *reinterpret_cast<u32x4*>(dst + 8) = g2_decode<1>(w0, lut, lb);
-      *reinterpret_cast<u32x4*>(dst + 16) = g2_decode<0>(w1, lut, lb);
-      *reinterpret_cast<u32x4*>(dst + 24) = g2_decode<1>(w1, lut, lb);
+#pragma unroll
+      for (int op = 0; op < 4; ++op) *reinterpret_cast<u32x4*>(dst + 8 * op) = F::decode32(creg, tab, op);
     };
 
     f32x16 acc[2][2];
@@ -183,7 +168,7 @@ __global__ __launch_bounds__(256, 2) void w2_gemm_kernel(
           const float gt = acc[a][0][i], up = acc[a][1][i];
           const float hv = __fdividef(gt, 1.0f + __expf(-gt)) * up;
           const int col = 64 * nt_i + 32 * wn + (lane & 31);
-          reinterpret_cast<uint16_t*>(out)[r * width + 16 * (col >> 4) + g_kpos16(col & 15)] =
+          reinterpret_cast<uint16_t*>(out)[r * width + 32 * (col >> 5) + F::pos32(col & 31)] =
               (uint16_t)f32_to_bf16_rne(hv);
         } else {
 #pragma unroll
@@ -196,42 +181,48 @@ __global__ __launch_bounds__(256, 2) void w2_gemm_kernel(
   }
 }
 
-static bool g_gemm_attr_set[2] = {false, false};
-
-template <int FC>
-static hipError_t launch_gemm(const uint32_t* codes, const uint16_t* scales, int rows, int K,
-                              int width, int ktop, const uint16_t* asrc, const int32_t* perm,
+template <class F, int FC>
+static hipError_t launch_gemm(const void* codes, const void* scales, int rows, int K, int width,
+                              int ktop, const uint16_t* asrc, const int32_t* perm,
                               const int32_t* plan, uint32_t asrc_bytes, int64_t tasks, void* out,
                               hipStream_t s) {
-  if (!g_gemm_attr_set[FC - 1]) {
-    hipError_t e = hipFuncSetAttribute((const void*)w2_gemm_kernel<FC>,
+  // dynamic LDS above 64 KB must be allowed once per kernel instance
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_kernel<F, FC>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
     if (e != hipSuccess) return e;
-    g_gemm_attr_set[FC - 1] = true;
+    attr_set = true;
   }
   const int64_t cap = 256 * 2;
   const int grid = (int)(tasks < cap ? (tasks > 0 ? tasks : 1) : cap);
-  w2_gemm_kernel<FC><<<grid, 256, kGemmLds, s>>>(codes, scales, rows, K, width, ktop, asrc, perm,
-                                                 plan, asrc_bytes, out);
+  gemm_kernel<F, FC><<<grid, 256, kGemmLds, s>>>((const uint8_t*)codes, (const uint8_t*)scales, rows, K,
+                                                 width, ktop, asrc, perm, plan, asrc_bytes, out);
   return hipGetLastError();
 }
 
 hipError_t launch_lowbit_gemm_fc1(const LowbitWeights& w, int H, int I, int k, const uint16_t* xp,
                                   const int32_t* perm, const int32_t* plan, int max_items, int T,
                                   uint16_t* hbuf, hipStream_t s) {
-  if (w.fmt != 1) return hipErrorInvalidValue;
-  return launch_gemm<1>((const uint32_t*)w.w1_codes, (const uint16_t*)w.w1_scales, 2 * I, H, I, k,
-                        xp, perm, plan, (uint32_t)((size_t)T * H * 2),
-                        (int64_t)max_items * (I / 64), hbuf, s);
+  const uint32_t xb = (uint32_t)((size_t)T * H * 2);
+  const int64_t tasks = (int64_t)max_items * (I / 64);
+  if (w.fmt == W2Fmt::kId)
+    return launch_gemm<W2Fmt, 1>(w.w1_codes, w.w1_scales, 2 * I, H, I, k, xp, perm, plan, xb, tasks, hbuf, s);
+  if (w.fmt == W3Fmt::kId)
+    return launch_gemm<W3Fmt, 1>(w.w1_codes, w.w1_scales, 2 * I, H, I, k, xp, perm, plan, xb, tasks, hbuf, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_lowbit_gemm_fc2(const LowbitWeights& w, int H, int I, int k,
                                   const uint16_t* hbuf, const int32_t* plan, int max_items, int T,
                                   float* y, hipStream_t s) {
-  if (w.fmt != 1) return hipErrorInvalidValue;
-  return launch_gemm<2>((const uint32_t*)w.w2_codes, (const uint16_t*)w.w2_scales, H, I, H, 1, hbuf,
-                        nullptr, plan, (uint32_t)((size_t)T * k * I * 2),
-                        (int64_t)max_items * (H / kBN), y, s);
+  const uint32_t hb = (uint32_t)((size_t)T * k * I * 2);
+  const int64_t tasks = (int64_t)max_items * (H / kBN);
+  if (w.fmt == W2Fmt::kId)
+    return launch_gemm<W2Fmt, 2>(w.w2_codes, w.w2_scales, H, I, H, 1, hbuf, nullptr, plan, hb, tasks, y, s);
+  if (w.fmt == W3Fmt::kId)
+    return launch_gemm<W3Fmt, 2>(w.w2_codes, w.w2_scales, H, I, H, 1, hbuf, nullptr, plan, hb, tasks, y, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace bitmoe

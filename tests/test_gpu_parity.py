@@ -25,10 +25,12 @@ def L():
 
 
 # ------------------------------------------------------------------ decoded weights
-@pytest.mark.parametrize("name,experts", [("tiny", [0, 5, 7]), ("decode", [0, 383])])
-def test_debug_dequant_bit_exact(L, name, experts):
-    sp, dw = device_layer(name)
-    lay = oracle_layer(name)
+@pytest.mark.parametrize("name,experts,override", [("tiny", [0, 5, 7], {}), ("decode", [0, 383], {}),
+                                                   ("w3", [0, 3, 15], {"E": 16}),
+                                                   ("w3", [2, 7], {"E": 8, "k": 2, "H": 256, "I": 512})])
+def test_debug_dequant_bit_exact(L, name, experts, override):
+    sp, dw = device_layer(name, **override)
+    lay = oracle_layer(name, **override)
     for e in experts:
         for which in (1, 2):
             got = host(L.moe_debug_dequant(dw, e, which)).astype(np.float64)
@@ -142,6 +144,21 @@ def test_layer_decode_shape_gemm_path(L, T, sample):
 @pytest.mark.parametrize("T,sample", [(8192, [0, 4097, 8191])])
 def test_layer_prefill(L, T, sample):
     _check_layer(L, "prefill", T, sample)
+
+
+# 3-bit experts: a small variant (many T, both kernels) and the full 512-expert shape
+W3_SMALL = {"E": 8, "k": 2, "H": 256, "I": 512}
+
+
+@pytest.mark.parametrize("T", [1, 5, 16, 37, 128, 300])
+def test_layer_w3_small(L, T):
+    _check_layer(L, "w3", T, **W3_SMALL)
+
+
+@pytest.mark.parametrize("T,sample", [(1, None), (8, None), (64, [0, 17, 63]), (512, [0, 255, 511]),
+                                      (4096, [0, 2048, 4095])])
+def test_layer_w3(L, T, sample):
+    _check_layer(L, "w3", T, sample)
 
 
 def test_layer_deterministic(L):
