@@ -144,7 +144,7 @@ def measure(sp: dict, dw, T: int, steps: int, warmup: int, flush_between: bool =
     ws_f = torch.empty(max(1, L.moe_expert_ffn_ws_bytes(dw, T, k)), dtype=torch.uint8, device=dev)
     y = torch.empty((R, H), dtype=torch.float32, device=dev)
     out = torch.empty((T, H), dtype=torch.int16, device=dev)
-    n_stages = L.moe_expert_ffn_num_stages(dw, T, k)
+    n_stages = L.moe_expert_ffn_num_stages(dw, T, k, ws_f.numel())
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB, read to evict caches
     stream = torch.cuda.current_stream()
 
@@ -226,6 +226,7 @@ def measure(sp: dict, dw, T: int, steps: int, warmup: int, flush_between: bool =
                    "cache_flush_between_steps": flush_between},
         "roofline": roof,
         "stages_ms": {"route+permute+prepare+combine": ms - fc1_ms - fc2_ms, "fc1": fc1_ms, "fc2": fc2_ms},
+        "ffn_stage_ms": [float(np.mean(v)) for v in stage_ms],
         "weight_GBps_fc1_fc2": (w1b + w2b) / ((fc1_ms + fc2_ms) * 1e-3) / 1e9,
         "ffn_TFLOPs_fc1_fc2": all_flops / ((fc1_ms + fc2_ms) * 1e-3) / 1e12,
         "ms_per_step_min": float(np.min(step_ms)),

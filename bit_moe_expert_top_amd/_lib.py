@@ -41,7 +41,7 @@ _SIGS = {
     "moe_permute": (_i32, [_p, _i32, _i32, _i32, _p, _p, _p, _p, _p, _sz, _p]),
     "moe_expert_ffn_ws_bytes": (_sz, [ctypes.POINTER(MoeWeights), _i32, _i32, _i32]),
     "moe_expert_ffn": (_i32, [ctypes.POINTER(MoeWeights), _p, _i32, _i32, _p, _p, _p, _p, _p, _sz, _p]),
-    "moe_expert_ffn_num_stages": (_i32, [ctypes.POINTER(MoeWeights), _i32, _i32]),
+    "moe_expert_ffn_num_stages": (_i32, [ctypes.POINTER(MoeWeights), _i32, _i32, _sz]),
     "moe_expert_ffn_stage": (_i32, [ctypes.POINTER(MoeWeights), _p, _i32, _i32, _p, _p, _p, _p, _p, _sz, _i32,
                                     _p]),
     "moe_combine": (_i32, [_p, _p, _p, _i32, _i32, _i32, _p, _i32, _p]),
@@ -155,8 +155,8 @@ def moe_expert_ffn(w: DeviceWeights, x: torch.Tensor, k: int, counts, offsets, p
     return y_perm
 
 
-def moe_expert_ffn_num_stages(w: DeviceWeights, T: int, k: int) -> int:
-    return lib.moe_expert_ffn_num_stages(ctypes.byref(w.c), T, k)
+def moe_expert_ffn_num_stages(w: DeviceWeights, T: int, k: int, ws_bytes: int) -> int:
+    return lib.moe_expert_ffn_num_stages(ctypes.byref(w.c), T, k, ws_bytes)
 
 
 def moe_expert_ffn_stage(w: DeviceWeights, x: torch.Tensor, k: int, counts, offsets, perm, y_perm, ws,
@@ -203,10 +203,11 @@ def moe_debug_dequant(w: DeviceWeights, e: int, which: int):
     return out
 
 
-def layer_forward(w: DeviceWeights, logits: torch.Tensor, x: torch.Tensor, k: int, out_fp32: bool = True):
+def layer_forward(w: DeviceWeights, logits: torch.Tensor, x: torch.Tensor, k: int, out_fp32: bool = True,
+                  fp8_slots: int | None = None):
     """The four calls in order; returns every intermediate (for tests and the bench)."""
     ids, gw = moe_route(logits, k)
     counts, offsets, perm, inv = moe_permute(ids, w.E)
-    y = moe_expert_ffn(w, x, k, counts, offsets, perm)
+    y = moe_expert_ffn(w, x, k, counts, offsets, perm, fp8_slots=fp8_slots)
     out = moe_combine(y, inv, gw, out_fp32=out_fp32)
     return dict(ids=ids, gates=gw, counts=counts, offsets=offsets, perm=perm, inv=inv, y_perm=y, out=out)

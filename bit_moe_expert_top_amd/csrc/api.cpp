@@ -24,11 +24,19 @@ constexpr int kStreamChunk = 32;
 // Batches of at least this many tokens run the grouped-GEMM kernels (prefill shape).
 constexpr int kGemmMinTokens = 128;
 
+// Hot experts are computed by the FP8 grouped GEMM on items of this many rows.
+constexpr int kHotChunk = 128;
+
 struct FfnLayout {
   bool gemm;
   int chunk;
   int64_t max_items;
-  size_t plan_off, xp_off, h_off, total;
+  size_t plan_off, xp_off, h_off;
+  // hot experts (n_hot > 0)
+  int64_t hot_max_items;
+  size_t hot_plan_off, xq_off, xqs_off, hq_off, hqs_off, slots_off;
+  size_t slot_bytes;
+  size_t fixed;  // bytes before the FP8 slots
 };
 
 FfnLayout ffn_layout(const moe_weights* w, int T, int k) {
@@ -44,8 +52,33 @@ FfnLayout ffn_layout(const moe_weights* w, int T, int k) {
   off = align256(off + (size_t)T * w->H * 2);
   L.h_off = off;  // h (bf16, k-slot order), R rows
   off = align256(off + (size_t)R * w->I * 2);
-  L.total = off;
+  L.hot_max_items = 0;
+  L.hot_plan_off = L.xq_off = L.xqs_off = L.hq_off = L.hqs_off = L.slots_off = off;
+  L.slot_bytes = 0;
+  if (w->n_hot > 0) {
+    L.hot_max_items = (R + kHotChunk - 1) / kHotChunk + (R < w->n_hot ? R : w->n_hot);
+    L.hot_plan_off = off;
+    off = align256(off + plan_bytes(L.hot_max_items));
+    L.xq_off = off;  // MXFP8 x: elements T x H, scales T x H/32
+    off = align256(off + (size_t)T * w->H);
+    L.xqs_off = off;
+    off = align256(off + (size_t)T * (w->H / 32));
+    L.hq_off = off;  // MXFP8 h of hot rows: R x I, scales R x I/32
+    off = align256(off + (size_t)R * w->I);
+    L.hqs_off = off;
+    off = align256(off + (size_t)R * (w->I / 32));
+    L.slots_off = off;
+    L.slot_bytes = (size_t)hot_layout(w->H, w->I).slot_bytes;
+  }
+  L.fixed = off;
   return L;
+}
+
+// FP8 slots that fit in ws_bytes (capped at n_hot); 0 if none fits or there is no hot set.
+int ffn_slots(const moe_weights* w, const FfnLayout& L, size_t ws_bytes) {
+  if (w->n_hot <= 0 || ws_bytes < L.fixed) return 0;
+  const size_t s = (ws_bytes - L.fixed) / L.slot_bytes;
+  return (int)(s < (size_t)w->n_hot ? s : (size_t)w->n_hot);
 }
 
 moe_status check_weights(const moe_weights* w) {
@@ -59,6 +92,17 @@ moe_status check_weights(const moe_weights* w) {
                        !w->hot_w2_scales))
     return MOE_ERR_INVALID_ARG;
   return MOE_OK;
+}
+
+HotWeights hot(const moe_weights* w) {
+  HotWeights h;
+  h.n_hot = w->n_hot;
+  h.hot_ids = w->hot_ids;
+  h.w1_codes = static_cast<const uint8_t*>(w->hot_w1_codes);
+  h.w1_scales = static_cast<const uint8_t*>(w->hot_w1_scales);
+  h.w2_codes = static_cast<const uint8_t*>(w->hot_w2_codes);
+  h.w2_scales = static_cast<const uint8_t*>(w->hot_w2_scales);
+  return h;
 }
 
 LowbitWeights lowbit(const moe_weights* w) {
@@ -120,9 +164,11 @@ moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
 }
 
 size_t moe_expert_ffn_ws_bytes(const moe_weights* w, int32_t T, int32_t k, int32_t fp8_slots) {
-  (void)fp8_slots;
   if (check_weights(w) != MOE_OK || T <= 0 || k <= 0) return 0;
-  return ffn_layout(w, T, k).total;
+  const FfnLayout L = ffn_layout(w, T, k);
+  if (w->n_hot == 0) return L.fixed;
+  const int s = (fp8_slots <= 0 || fp8_slots > w->n_hot) ? w->n_hot : fp8_slots;
+  return L.fixed + (size_t)s * L.slot_bytes;
 }
 
 namespace {
@@ -137,16 +183,27 @@ moe_status ffn_check(const moe_weights* w, const uint16_t* x, int32_t T, int32_t
   if ((int64_t)T * k >= ((int64_t)1 << 31)) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!x || !counts || !offsets || !perm || !y_perm) return MOE_ERR_INVALID_ARG;
-  if (w->n_hot != 0) return MOE_ERR_UNSUPPORTED;
-  if (!ws || ws_bytes < ffn_layout(w, T, k).total) return MOE_ERR_WORKSPACE;
+  const FfnLayout L = ffn_layout(w, T, k);
+  if (!ws || ws_bytes < L.fixed) return MOE_ERR_WORKSPACE;
+  if (w->n_hot > 0 && ffn_slots(w, L, ws_bytes) < 1) return MOE_ERR_WORKSPACE;
   return MOE_OK;
 }
 
-constexpr int kFfnStages = 3;  // prepare, FC1 + SwiGLU, FC2
+// Stages: 0 prepare (low-bit work list, x in k-slot order), 1 low-bit FC1 + SwiGLU, 2 low-bit
+// FC2; with a hot set, 3 hot prepare (hot work list, MXFP8 of x), then per batch of S hot
+// experts: convert into the slots, FP8 FC1 + SwiGLU + MXFP8 of h, FP8 FC2.
+constexpr int kLowbitStages = 3;
+
+int ffn_num_stages(const moe_weights* w, int T, int k, size_t ws_bytes) {
+  if (w->n_hot <= 0) return kLowbitStages;
+  const int S = ffn_slots(w, ffn_layout(w, T, k), ws_bytes);
+  if (S < 1) return kLowbitStages + 1;
+  return kLowbitStages + 1 + 3 * ((w->n_hot + S - 1) / S);
+}
 
 moe_status ffn_run_stage(const moe_weights* w, const uint16_t* x, int32_t T, int32_t k,
-                         const int32_t* offsets, const int32_t* perm, float* y_perm, void* ws,
-                         int stage, hipStream_t s) {
+                         const int32_t* counts, const int32_t* offsets, const int32_t* perm,
+                         float* y_perm, void* ws, size_t ws_bytes, int stage, hipStream_t s) {
   const FfnLayout L = ffn_layout(w, T, k);
   char* base = static_cast<char*>(ws);
   int32_t* plan = reinterpret_cast<int32_t*>(base + L.plan_off);
@@ -166,8 +223,29 @@ moe_status ffn_run_stage(const moe_weights* w, const uint16_t* x, int32_t T, int
       e = L.gemm ? launch_lowbit_gemm_fc2(lw, w->H, w->I, k, hbuf, plan, (int)L.max_items, T, y_perm, s)
                  : launch_lowbit_fc2(lw, w->E, w->H, w->I, k, hbuf, plan, (int)L.max_items, T, y_perm, s);
       break;
-    default:
-      return MOE_ERR_INVALID_ARG;
+    case 3:
+      e = launch_hot_prepare(offsets, w->E, kHotChunk, w->hot_ids, w->n_hot,
+                             reinterpret_cast<int32_t*>(base + L.hot_plan_off), x, T, w->H,
+                             reinterpret_cast<uint8_t*>(base + L.xq_off),
+                             reinterpret_cast<uint8_t*>(base + L.xqs_off), s);
+      break;
+    default: {
+      const int S = ffn_slots(w, L, ws_bytes);
+      const int b0 = ((stage - 4) / 3) * S, part = (stage - 4) % 3;
+      const int32_t* hplan = reinterpret_cast<const int32_t*>(base + L.hot_plan_off);
+      uint8_t* slots = reinterpret_cast<uint8_t*>(base + L.slots_off);
+      uint8_t* hq = reinterpret_cast<uint8_t*>(base + L.hq_off);
+      uint8_t* hqs = reinterpret_cast<uint8_t*>(base + L.hqs_off);
+      if (part == 0)
+        e = launch_hot_convert(hot(w), w->H, w->I, counts, b0, S, slots, s);
+      else if (part == 1)
+        e = launch_hot_fc1(w->H, w->I, k, T, hplan, (int)L.hot_max_items, b0, S, slots,
+                           reinterpret_cast<const uint8_t*>(base + L.xq_off),
+                           reinterpret_cast<const uint8_t*>(base + L.xqs_off), perm, hq, hqs, s);
+      else
+        e = launch_hot_fc2(w->H, w->I, (int64_t)T * k, hplan, (int)L.hot_max_items, b0, S, slots, hq, hqs,
+                           y_perm, s);
+    }
   }
   return from_hip(e);
 }
@@ -179,14 +257,16 @@ moe_status moe_expert_ffn(const moe_weights* w, const uint16_t* x, int32_t T, in
                           float* y_perm, void* ws, size_t ws_bytes, void* stream) {
   moe_status st = ffn_check(w, x, T, k, counts, offsets, perm, y_perm, ws, ws_bytes);
   if (st != MOE_OK || T == 0) return st;
-  for (int stage = 0; stage < kFfnStages && st == MOE_OK; ++stage)
-    st = ffn_run_stage(w, x, T, k, offsets, perm, y_perm, ws, stage, as_stream(stream));
+  const int n = ffn_num_stages(w, T, k, ws_bytes);
+  for (int stage = 0; stage < n && st == MOE_OK; ++stage)
+    st = ffn_run_stage(w, x, T, k, counts, offsets, perm, y_perm, ws, ws_bytes, stage, as_stream(stream));
   return st;
 }
 
-int32_t moe_expert_ffn_num_stages(const moe_weights* w, int32_t T, int32_t k) {
-  (void)w; (void)T; (void)k;
-  return kFfnStages;
+int32_t moe_expert_ffn_num_stages(const moe_weights* w, int32_t T, int32_t k, size_t ws_bytes) {
+  if (check_weights(w) != MOE_OK || T < 0 || k < 1) return 0;
+  if (T == 0) return 0;
+  return ffn_num_stages(w, T, k, ws_bytes);
 }
 
 moe_status moe_expert_ffn_stage(const moe_weights* w, const uint16_t* x, int32_t T, int32_t k,
@@ -195,8 +275,8 @@ moe_status moe_expert_ffn_stage(const moe_weights* w, const uint16_t* x, int32_t
                                 void* stream) {
   moe_status st = ffn_check(w, x, T, k, counts, offsets, perm, y_perm, ws, ws_bytes);
   if (st != MOE_OK || T == 0) return st;
-  if (stage < 0 || stage >= kFfnStages) return MOE_ERR_INVALID_ARG;
-  return ffn_run_stage(w, x, T, k, offsets, perm, y_perm, ws, stage, as_stream(stream));
+  if (stage < 0 || stage >= ffn_num_stages(w, T, k, ws_bytes)) return MOE_ERR_INVALID_ARG;
+  return ffn_run_stage(w, x, T, k, counts, offsets, perm, y_perm, ws, ws_bytes, stage, as_stream(stream));
 }
 
 moe_status moe_combine(const float* y_perm, const int32_t* inv, const float* topk_w, int32_t T,
@@ -211,14 +291,18 @@ moe_status moe_combine(const float* y_perm, const int32_t* inv, const float* top
 
 moe_status moe_mxfp4_to_fp8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int32_t K,
                             uint8_t* elems, uint8_t* out_scales, void* stream) {
-  (void)codes; (void)scales; (void)rows; (void)K; (void)elems; (void)out_scales; (void)stream;
-  return MOE_ERR_UNSUPPORTED;
+  if (rows < 0 || K <= 0 || K % 32) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (!codes || !scales || !elems || !out_scales) return MOE_ERR_INVALID_ARG;
+  return from_hip(launch_mxfp4_to_fp8(codes, scales, rows, K, elems, out_scales, as_stream(stream)));
 }
 
 moe_status moe_mxfp8_quantize(const uint16_t* x, int64_t rows, int32_t K, uint8_t* elems,
                               uint8_t* scales, void* stream) {
-  (void)x; (void)rows; (void)K; (void)elems; (void)scales; (void)stream;
-  return MOE_ERR_UNSUPPORTED;
+  if (rows < 0 || K <= 0 || K % 32) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (!x || !elems || !scales) return MOE_ERR_INVALID_ARG;
+  return from_hip(launch_mxfp8_quantize(x, rows, K, elems, scales, as_stream(stream)));
 }
 
 moe_status moe_debug_dequant(const moe_weights* w, int32_t e, int32_t which, float* out,

@@ -16,6 +16,7 @@
 #include "common.h"
 #include "kernels.h"
 #include "lowbit_fmt.h"
+#include "plan.h"
 
 namespace bitmoe {
 
@@ -73,31 +74,7 @@ __global__ __launch_bounds__(1024) void prepare_kernel(const int32_t* __restrict
     }
     return;
   }
-  // block 0: the work list
-  __shared__ int scan_tmp[1024 / kWave + 1];
-  __shared__ int16_t slot_of[1024];
-  for (int e = threadIdx.x; e < E; e += 1024) slot_of[e] = -1;
-  __syncthreads();
-  for (int s = threadIdx.x; s < n_hot; s += 1024) slot_of[hot_ids[s]] = (int16_t)s;
-  __syncthreads();
-  int4* items = reinterpret_cast<int4*>(plan + 4);
-  int running = 0;
-  for (int e0 = 0; e0 < E; e0 += 1024) {
-    const int e = e0 + threadIdx.x;
-    int cnt = 0, slot = -1;
-    if (e < E) {
-      slot = slot_of[e];
-      cnt = offsets[e + 1] - offsets[e];
-      if ((slot >= 0) != (want_hot != 0)) cnt = 0;
-    }
-    const int nch = (cnt + chunk - 1) / chunk;
-    int tot;
-    const int ex = block_exclusive_scan<1024>(nch, scan_tmp, &tot);
-    for (int c = 0; c < nch; ++c)
-      items[running + ex + c] = make_int4(e, offsets[e] + c * chunk, min(chunk, cnt - c * chunk), slot);
-    running += tot;
-  }
-  if (threadIdx.x == 0) plan[0] = running;
+  build_plan(offsets, E, chunk, hot_ids, n_hot, want_hot, plan);
 }
 
 hipError_t launch_prepare(const int32_t* offsets, int E, int chunk_rows, const int32_t* hot_ids,

@@ -59,6 +59,40 @@ hipError_t launch_lowbit_gemm_fc2(const LowbitWeights& w, int H, int I, int k,
                                   const uint16_t* hbuf, const int32_t* plan, int max_items, int T,
                                   float* y, hipStream_t s);
 
+// ---- hot experts (MXFP4 held, converted to FP8 into workspace slots, MXFP8 activations)
+struct HotWeights {
+  int n_hot;
+  const int32_t* hot_ids;
+  const uint8_t* w1_codes;   // [n_hot][2I][H/2]
+  const uint8_t* w1_scales;  // [n_hot][2I][H/32]
+  const uint8_t* w2_codes;   // [n_hot][H][I/2]
+  const uint8_t* w2_scales;  // [n_hot][H][I/32]
+};
+// Byte layout of one workspace slot: the FP8 image of one hot expert.
+struct HotLayout {
+  int64_t w1_off, w1s_off, w2_off, w2s_off, slot_bytes;
+};
+HotLayout hot_layout(int H, int I);
+
+hipError_t launch_mxfp8_quantize(const uint16_t* x, int64_t rows, int K, uint8_t* elems,
+                                 uint8_t* scales, hipStream_t s);
+hipError_t launch_mxfp4_to_fp8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int K,
+                               uint8_t* elems, uint8_t* out_scales, hipStream_t s);
+// Hot work list (items of <= chunk_rows rows of hot experts) and MXFP8 of x, in one launch.
+hipError_t launch_hot_prepare(const int32_t* offsets, int E, int chunk_rows, const int32_t* hot_ids,
+                              int n_hot, int32_t* plan, const uint16_t* x, int T, int H, uint8_t* xq,
+                              uint8_t* xqs, hipStream_t s);
+// Convert hot experts b0 .. b0+S-1 that have rows (counts > 0) into slots 0 .. S-1.
+hipError_t launch_hot_convert(const HotWeights& hw, int H, int I, const int32_t* counts, int b0,
+                              int S, uint8_t* slots, hipStream_t s);
+// FP8 grouped GEMMs over the hot work list, for the experts in slots b0 .. b0+S-1.
+hipError_t launch_hot_fc1(int H, int I, int k, int T, const int32_t* hot_plan, int max_items, int b0,
+                          int S, const uint8_t* slots, const uint8_t* xq, const uint8_t* xqs,
+                          const int32_t* perm, uint8_t* hq, uint8_t* hqs, hipStream_t s);
+hipError_t launch_hot_fc2(int H, int I, int64_t R, const int32_t* hot_plan, int max_items, int b0,
+                          int S, const uint8_t* slots, const uint8_t* hq, const uint8_t* hqs,
+                          float* y, hipStream_t s);
+
 hipError_t launch_debug_dequant(const LowbitWeights& w, int E, int H, int I, int e, int which,
                                 float* out, hipStream_t s);
 

@@ -1,0 +1,41 @@
+// The FFN work list, built on the device from the grouping offsets (no host round trip).
+#pragma once
+
+#include "common.h"
+
+namespace bitmoe {
+
+// Run by one block of 1024 threads.  plan[0] = number of items; then int4 items
+// {expert, first grouped row, rows, hot slot or -1}: the rows of every expert of the
+// requested kind (low-bit experts, or hot experts if want_hot) split into items of at most
+// `chunk` rows, experts in id order.
+__device__ __forceinline__ void build_plan(const int32_t* __restrict__ offsets, int E, int chunk,
+                                           const int32_t* __restrict__ hot_ids, int n_hot, int want_hot,
+                                           int32_t* __restrict__ plan) {
+  __shared__ int scan_tmp[1024 / kWave + 1];
+  __shared__ int16_t slot_of[1024];
+  for (int e = threadIdx.x; e < E; e += 1024) slot_of[e] = -1;
+  __syncthreads();
+  for (int s = threadIdx.x; s < n_hot; s += 1024) slot_of[hot_ids[s]] = (int16_t)s;
+  __syncthreads();
+  int4* items = reinterpret_cast<int4*>(plan + 4);
+  int running = 0;
+  for (int e0 = 0; e0 < E; e0 += 1024) {
+    const int e = e0 + threadIdx.x;
+    int cnt = 0, slot = -1;
+    if (e < E) {
+      slot = slot_of[e];
+      cnt = offsets[e + 1] - offsets[e];
+      if ((slot >= 0) != (want_hot != 0)) cnt = 0;
+    }
+    const int nch = (cnt + chunk - 1) / chunk;
+    int tot;
+    const int ex = block_exclusive_scan<1024>(nch, scan_tmp, &tot);
+    for (int c = 0; c < nch; ++c)
+      items[running + ex + c] = make_int4(e, offsets[e] + c * chunk, min(chunk, cnt - c * chunk), slot);
+    running += tot;
+  }
+  if (threadIdx.x == 0) plan[0] = running;
+}
+
+}  // namespace bitmoe

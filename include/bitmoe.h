@@ -127,9 +127,12 @@ moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
  *   x        bf16 (u16 bits) [T][H]
  *   counts, offsets, perm   as produced by moe_permute for the same topk_ids
  *   y_perm   f32[R][H]   out (row r = grouped row r)
- *   ws       workspace of at least moe_expert_ffn_ws_bytes(w, T, k, fp8_slots) bytes; the
- *            number of FP8 slots used is the largest that fits, capped at n_hot, and the hot
- *            experts are converted and computed in batches of that many.
+ *   ws       workspace of at least moe_expert_ffn_ws_bytes(w, T, k, fp8_slots) bytes
+ *            (fp8_slots <= 0 or > n_hot means n_hot; ignored without a hot set).  A slot holds
+ *            the FP8 image of one hot expert (3 H I * 33/32 bytes); the number of slots used is
+ *            the largest that fits in ws_bytes, capped at n_hot, and the hot experts are
+ *            converted and computed in batches of that many (at least one slot must fit).
+ *   hot_ids  must be distinct expert ids in [0, E) (not checked: device memory).
  * Requirements: H % 256 == 0, I % 256 == 0, H and I <= 16384; fmt W2 or W3.
  * Errors: INVALID_ARG, UNSUPPORTED (format/shape not built), WORKSPACE. */
 size_t moe_expert_ffn_ws_bytes(const moe_weights* w, int32_t T, int32_t k, int32_t fp8_slots);
@@ -138,13 +141,16 @@ moe_status moe_expert_ffn(const moe_weights* w, const uint16_t* x, int32_t T, in
                           float* y_perm, void* ws, size_t ws_bytes, void* stream);
 
 /* moe_expert_ffn_stage -- run one stage of moe_expert_ffn.  Calling stages 0 .. n-1, with
- * n = moe_expert_ffn_num_stages(w, T, k), in order on one stream with the same arguments and
- * workspace is exactly moe_expert_ffn.  Each stage is a single kernel launch, so a caller can
- * time the kernels one by one (HIP events on `stream`) or interleave other work between them.
- * Stages of a low-bit layer: 0 = work list from offsets and x in MFMA operand order,
- * 1 = FC1 + SwiGLU (h into the workspace), 2 = FC2 (y_perm).
+ * n = moe_expert_ffn_num_stages(w, T, k, ws_bytes), in order on one stream with the same
+ * arguments and workspace is exactly moe_expert_ffn.  Each stage is a single kernel launch, so
+ * a caller can time the kernels one by one (HIP events on `stream`) or interleave other work.
+ * Stages: 0 = low-bit work list and x in the MFMA k-slot order, 1 = low-bit FC1 + SwiGLU,
+ * 2 = low-bit FC2.  With a hot set (n_hot > 0): 3 = hot work list and MXFP8 of x, then for
+ * each batch of S hot experts (S = FP8 slots in the workspace): convert the batch's hot
+ * experts that have rows into the slots, FP8 FC1 + SwiGLU + MXFP8 of h, FP8 FC2.
+ * num_stages returns 0 for invalid arguments or T = 0.
  * Errors: as moe_expert_ffn; INVALID_ARG for a stage out of range. */
-int32_t moe_expert_ffn_num_stages(const moe_weights* w, int32_t T, int32_t k);
+int32_t moe_expert_ffn_num_stages(const moe_weights* w, int32_t T, int32_t k, size_t ws_bytes);
 moe_status moe_expert_ffn_stage(const moe_weights* w, const uint16_t* x, int32_t T, int32_t k,
                                 const int32_t* counts, const int32_t* offsets, const int32_t* perm,
                                 float* y_perm, void* ws, size_t ws_bytes, int32_t stage,

@@ -9,7 +9,7 @@ import moegen
 from oracle import formats as OF
 from oracle import moe as OM
 
-from _helpers import (TOL_BF16, bf16_bits_host, device_layer, host, layer_arrays, max_err_over_rms,
+from _helpers import (TOL_BF16, TOL_FP8, bf16_bits_host, device_layer, host, layer_arrays, max_err_over_rms,
                       oracle_layer, to_dev)
 
 pytestmark = pytest.mark.gpu
@@ -91,12 +91,13 @@ def test_combine_bf16_is_rne_of_fp32(L):
 
 
 # ------------------------------------------------------------------ the whole layer
-def _check_layer(L, name, T, sample_tokens=None, **override):
+def _check_layer(L, name, T, sample_tokens=None, fp8_slots=None, **override):
     sp, dw = device_layer(name, **override)
     lay = oracle_layer(name, **override)
     b = moegen.batch(sp, T)
     k = sp["k"]
-    res = L.layer_forward(dw, to_dev(b["logits"]), to_dev(b["x"]), k, out_fp32=True)
+    tol = TOL_FP8 if sp["n_hot"] > 0 else TOL_BF16
+    res = L.layer_forward(dw, to_dev(b["logits"]), to_dev(b["x"]), k, out_fp32=True, fp8_slots=fp8_slots)
     ids, gates = OM.route(b["logits"], k)
     counts, offsets, perm, inv = OM.permute(ids, sp["E"])
     np.testing.assert_array_equal(host(res["ids"]), ids)
@@ -111,9 +112,9 @@ def _check_layer(L, name, T, sample_tokens=None, **override):
     got = host(res["out"])[toks]
     err = max_err_over_rms(got, out)
     print(f"{name} T={T}: max|err|/rms = {err:.4g}", flush=True)
-    assert err <= TOL_BF16
+    assert err <= tol
     rows = np.concatenate([np.arange(offsets[e], offsets[e + 1]) for e in experts])
-    assert max_err_over_rms(host(res["y_perm"])[rows], y[rows]) <= TOL_BF16
+    assert max_err_over_rms(host(res["y_perm"])[rows], y[rows]) <= tol
     # bf16 output is the RNE of the same fp32 sums
     o16 = L.moe_combine(res["y_perm"], res["inv"], res["gates"], out_fp32=False)
     ref16 = res["out"].to(torch.bfloat16).view(torch.int16)
@@ -159,6 +160,54 @@ def test_layer_w3_small(L, T):
                                       (4096, [0, 2048, 4095])])
 def test_layer_w3(L, T, sample):
     _check_layer(L, "w3", T, sample)
+
+
+# ------------------------------------------------------------------ hot experts (MXFP4 -> FP8)
+def test_mxfp4_to_fp8_bit_exact(L):
+    r = np.random.default_rng(11)
+    codes = r.integers(0, 256, size=(37, 160), dtype=np.uint8)
+    codes[0, :16] = np.arange(16, dtype=np.uint8) * 17  # every nibble in both positions
+    scales = r.integers(0, 256, size=(37, 10), dtype=np.uint8)
+    elems, sc = L.moe_mxfp4_to_fp8(to_dev(codes), to_dev(scales))
+    we, ws = OF.mxfp4_to_fp8(codes, scales)
+    np.testing.assert_array_equal(host(elems), we)
+    np.testing.assert_array_equal(host(sc), ws)
+
+
+def test_mxfp8_quantize_bit_exact(L):
+    r = np.random.default_rng(12)
+    rows, K = 64, 256
+    x = moegen._f32_to_bf16_bits((r.standard_normal((rows, K)) * np.exp2(r.integers(-20, 20, (rows, 1)))).astype(np.float32))
+    x[0, :32] = 0                                   # all-zero block -> scale byte 0
+    x[0, 32:64] = 0x8000                            # all -0
+    x[1, :32] = r.integers(1, 0x80, 32)             # bf16 subnormals
+    x[1, 32:64] = 0x7F7F                            # the largest bf16
+    x[2, :32] = moegen._f32_to_bf16_bits(np.float32(1.8125) * np.ones(32, np.float32))  # ties at the top
+    x[2, 40] = moegen._f32_to_bf16_bits(np.float32(-448.0 * 1.0625))
+    x[3, :] = moegen._f32_to_bf16_bits(np.float32(1e-3) * r.standard_normal(K).astype(np.float32))
+    elems, sc = L.moe_mxfp8_quantize(to_dev(x))
+    we, ws = OF.mxfp8_quantize(OF.bf16_value(x))
+    np.testing.assert_array_equal(host(sc), ws)
+    np.testing.assert_array_equal(host(elems), we)
+
+
+MIXED_SMALL = {"E": 16, "k": 4, "H": 256, "I": 512, "n_hot": 4}
+
+
+@pytest.mark.parametrize("T", [1, 16, 100, 300])
+def test_layer_mixed_small(L, T):
+    _check_layer(L, "mixed", T, **MIXED_SMALL)
+
+
+def test_layer_mixed_small_fewer_slots_than_hot_experts(L):
+    a = _check_layer(L, "mixed", 200, fp8_slots=1, **MIXED_SMALL)
+    b = _check_layer(L, "mixed", 200, fp8_slots=3, **MIXED_SMALL)
+    assert torch.equal(a["out"], b["out"])
+
+
+@pytest.mark.parametrize("T,sample", [(64, [0, 31, 63]), (4096, [0, 1500, 4095])])
+def test_layer_mixed(L, T, sample):
+    _check_layer(L, "mixed", T, sample)
 
 
 def test_layer_deterministic(L):

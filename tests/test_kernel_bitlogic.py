@@ -209,3 +209,108 @@ def test_w3_decode_every_finite_scale_byte_and_golden_fields():
             got = emulate_w3_row(codes, np.array([b], np.uint8))
             want = OF.dequant_w3(codes[None, :], np.array([[b]], np.uint8))[0]
             np.testing.assert_array_equal(got, want, err_msg=f"scale byte {b:#x}")
+
+
+def _header_table(name):
+    import os
+    import re
+    src = open(os.path.join(os.path.dirname(__file__), "..", "bit_moe_expert_top_amd", "csrc", "lowbit_fmt.h")).read()
+    m = re.search(name + r"\[32\]\s*=\s*\{([^}]*)\}", src)
+    return [int(v) for v in m.group(1).replace("\n", " ").split(",")]
+
+
+def test_device_slot_tables_match_the_emulated_decode():
+    slot_k, pos = _header_table("kW3SlotK"), _header_table("kW3Pos")
+    assert slot_k == SLOT3
+    assert [pos[c] for c in slot_k] == list(range(32))
+
+
+# --- MX formats (mx_fmt.h): the e2m1 -> e4m3 byte table and the integer e4m3 encoder ---
+E2M1_TO_E4M3_LO, E2M1_TO_E4M3_HI = 0x3C383000, 0x4C484440
+
+
+def e2m1x8_to_e4m3(w):
+    lo, hi = w & 0x0F0F0F0F, (w >> 4) & 0x0F0F0F0F
+    elo = v_perm_b32(E2M1_TO_E4M3_HI, E2M1_TO_E4M3_LO, lo & 0x07070707) | ((lo & 0x08080808) << 4)
+    ehi = v_perm_b32(E2M1_TO_E4M3_HI, E2M1_TO_E4M3_LO, hi & 0x07070707) | ((hi & 0x08080808) << 4)
+    return v_perm_b32(ehi, elo, 0x05010400), v_perm_b32(ehi, elo, 0x07030602)
+
+
+def test_e2m1_conversion_table_matches_oracle():
+    r = np.random.default_rng(5)
+    codes = r.integers(0, 256, size=(3, 64), dtype=np.uint8)
+    codes[0, :16] = np.arange(0, 256, 16, dtype=np.uint8) | np.arange(16, dtype=np.uint8)  # every nibble
+    want, _ = OF.mxfp4_to_fp8(codes, np.zeros((3, 4), np.uint8))
+    for row in range(3):
+        words = codes[row].view(np.uint32)
+        got = []
+        for w in words.tolist():
+            o0, o1 = e2m1x8_to_e4m3(w)
+            got += [(o0 >> (8 * i)) & 0xFF for i in range(4)] + [(o1 >> (8 * i)) & 0xFF for i in range(4)]
+        assert got == want[row].tolist()
+
+
+def e4m3_mag_rne(M, F):
+    m = M.bit_length() - 1
+    fl = m + F
+    if fl > 8:
+        return 0x7E
+    if fl >= -6:
+        sh, ebase = m - 3, fl + 7
+    else:
+        sh, ebase = -(F + 9), 0
+    if sh <= 0:
+        q = M << (-sh)
+    elif sh > 25:
+        q = 0
+    else:
+        q, rem, half = M >> sh, M & ((1 << sh) - 1), 1 << (sh - 1)
+        q += 1 if (rem > half or (rem == half and q & 1)) else 0
+    if ebase == 0:
+        byte = q
+    else:
+        byte = (ebase + 1) << 3 if q == 16 else (ebase << 3) | (q - 8)
+    return min(byte, 0x7E)
+
+
+def bf16_to_e4m3_scaled(b, shared):
+    sgn, mag = (b >> 8) & 0x80, b & 0x7FFF
+    if mag == 0:
+        return sgn
+    eb, mb = mag >> 7, mag & 0x7F
+    M = (mb | 0x80) if eb else mb
+    E0 = eb - 134 if eb else -133
+    return sgn | e4m3_mag_rne(M, E0 - shared)
+
+
+def f32_to_e4m3_scaled(b, shared):
+    sgn, mag = (b >> 24) & 0x80, b & 0x7FFFFFFF
+    if mag == 0:
+        return sgn
+    eb, mb = mag >> 23, mag & 0x7FFFFF
+    M = (mb | 0x800000) if eb else mb
+    E0 = eb - 150 if eb else -149
+    return sgn | e4m3_mag_rne(M, E0 - shared)
+
+
+def test_integer_e4m3_encoder_matches_oracle_rne():
+    r = np.random.default_rng(6)
+    # bf16 patterns over the whole range (normals, subnormals, zeros), with shared exponents
+    bits = r.integers(0, 1 << 16, size=4000).astype(np.uint16)
+    bits = bits[((bits >> 7) & 0xFF) != 0xFF]  # finite only
+    shared = r.integers(-127, 128, size=bits.size)
+    vals = OF.bf16_value(bits) / np.exp2(shared.astype(np.float64))
+    want = OF.e4m3fn_encode(vals)
+    got = np.array([bf16_to_e4m3_scaled(int(b), int(s)) for b, s in zip(bits, shared)], np.uint8)
+    np.testing.assert_array_equal(got, want)
+    # fp32 patterns near the rounding boundaries of e4m3 (ties, saturation, subnormals)
+    grid = OF.e4m3fn_value(np.arange(0, 0x7F, dtype=np.uint8))
+    mids = np.concatenate([(grid[:-1] + grid[1:]) / 2, grid, [448.0, 464.0, 465.0, 479.0, 480.0, 1e4]])
+    mids = np.concatenate([mids, -mids])
+    f32 = mids.astype(np.float32)
+    for shared in (-3, 0, 5):
+        v = f32.astype(np.float64) * 2.0 ** shared
+        v32 = v.astype(np.float32)
+        want = OF.e4m3fn_encode(v32.astype(np.float64) / 2.0 ** shared)
+        got = np.array([f32_to_e4m3_scaled(int(b), shared) for b in v32.view(np.uint32)], np.uint8)
+        np.testing.assert_array_equal(got, want)
