@@ -195,7 +195,7 @@ def measure(sp: dict, dw, T: int, steps: int, warmup: int, flush_between: bool =
         # prefill-sized: FC1 is a grouped GEMM; algorithmic flops = 2 * R * (2I) * H
         fc1_flops = 2.0 * R * (2 * I) * H
         achieved = fc1_flops / (fc1_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": "moe_expert_ffn stage 1: FC1 + SwiGLU grouped GEMM (w2_gemm_kernel<1>)",
+        roof = {"bound": "mfma", "kernel": "moe_expert_ffn stage 1: FC1 + SwiGLU grouped GEMM (gemm_kernel<W2Fmt, 1>)",
                 "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / BF16_PEAK_TFLOPS, "alg_flops_per_launch": fc1_flops}
     else:
@@ -203,7 +203,7 @@ def measure(sp: dict, dw, T: int, steps: int, warmup: int, flush_between: bool =
         # token, reads x once and writes h once
         fc1_bytes = w1b + T * H * 2 + R * I * 2
         achieved = fc1_bytes / (fc1_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": "moe_expert_ffn stage 1: FC1 + SwiGLU weight streaming (w2_stream_kernel<1, G>)",
+        roof = {"bound": "hbm", "kernel": "moe_expert_ffn stage 1: FC1 + SwiGLU weight streaming (stream_kernel<W2Fmt, 1, G>)",
                 "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "alg_bytes_per_launch": fc1_bytes}
     roof["traffic"] = measured_traffic(workload)
@@ -258,7 +258,7 @@ def main():
     ap.add_argument("--layer", default="decode", help="decode | tiny")
     ap.add_argument("--T", type=int, default=64)
     ap.add_argument("--no-flush", action="store_true", help="do not flush caches between steps")
-    ap.add_argument("--cpu-tokens", type=int, default=8, help="tokens of the oracle's timed sample (0 = skip)")
+    ap.add_argument("--cpu-tokens", type=int, default=64, help="tokens of the oracle's timed sample (0 = skip)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after timing, run a plain copy of this many MiB (counter calibration)")
     args = ap.parse_args()

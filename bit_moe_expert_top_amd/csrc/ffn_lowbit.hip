@@ -97,19 +97,22 @@ constexpr int kRT = 4;  // 16-row A tiles per wave (64 weight rows)
 //     kbase + 256*G*c + 64*G*q + 64*s + [0, 64)
 // so over a super-step a lane covers 64*G consecutive k: its scales for the whole super-step
 // are contiguous bytes (one load), and its codes for step s are contiguous (one or two loads).
-// The token operand uses the same mapping, in the format's slot order.
+//
+// The token operand (B) of a step is staged in LDS once per workgroup and shared by its 4
+// waves: direct global -> LDS loads (16 bytes per lane, no registers), double buffered, one
+// barrier per step.  A stage holds, for each of the KS parts of K, the 16*NT token rows of the
+// item, each 256 k (512 bytes, the step's four 64-k pieces in quad order) with the 16-byte
+// chunks XOR-swizzled by the token index (conflict-free LDS reads).
+constexpr int kBStage = 4 * 16 * 512;  // the largest stage: KS = 4 x 16 tokens (or KS = 1 x 32)
+typedef __attribute__((address_space(3))) void lds_void;
 
-// Per-wave pipeline state: the codes of steps in a two-slot ring (issued two steps ahead),
-// the scales of the current and the next super-step, the token operand in double-buffered
-// batches of WB operand pairs, and the accumulators.
+// Per-wave pipeline state: the codes of steps in a two-slot ring (issued two steps ahead), the
+// scales of the current and the next super-step, and the accumulators.
 template <class F, int NT, int G>
 struct Pipe {
-  static constexpr int WB = NT == 1 ? 4 : 2;  // operand pairs per token batch
-  static constexpr int NBATCH = 4 / WB;       // batches per step
   static constexpr int SB = F::kStepScaleBytes * G;
   typename F::Codes cw[2][kRT];
   ScaleBytes<SB> sc[kRT], sc_next[kRT];
-  u32x4 b[2][WB][NT][2];
   f32x4 acc[kRT][NT];
 };
 
@@ -129,55 +132,59 @@ __device__ __forceinline__ void load_scales(Pipe<F, NT, G>& P, buf_rsrc rs, cons
     P.sc_next[t] = load_scale_bytes<Pipe<F, NT, G>::SB>(rs, soff[t] + F::scale_bytes(256u * G * (uint32_t)c));
 }
 
-// Token operand of batch wb of step `st`.  boff: byte offset of the lane's token row plus its
-// quad's k offset, or >= kOffNone for lanes past the item's rows (they read zeros).
-template <class F, int NT, int G>
-__device__ __forceinline__ void load_batch(Pipe<F, NT, G>& P, int buf, buf_rsrc rb,
-                                           const uint32_t* boff, int st, int wb) {
-  const uint32_t o = 512u * G * (uint32_t)(st / G) + 128u * (uint32_t)(st % G);
+// Direct loads of the token operand of step st into a stage buffer: round u of this wave
+// writes the 1 KB at stage + 16 * (256 u + 64 w).  doff: per-round source offsets (>= kOffNone
+// for chunks past the item's rows, which land as zeros).
+// `active` (wave-uniform) has bit u set for the rounds of this wave that hold a real token.
+template <int G>
+__device__ __forceinline__ void dma_b(buf_rsrc rb, uint8_t* stage, const uint32_t* doff, uint32_t active,
+                                      int wu, int st) {
+  const uint32_t ko = 2u * (256u * G * (uint32_t)(st / G) + 64u * (uint32_t)(st % G));
 #pragma unroll
-  for (int v = 0; v < Pipe<F, NT, G>::WB; ++v) {
-    const int j = wb * Pipe<F, NT, G>::WB + v;
-#pragma unroll
-    for (int bt = 0; bt < NT; ++bt) {
-      const uint32_t ob = boff[bt] + o + 32u * j;
-      P.b[buf][v][bt][0] = buf_load16(rb, ob);
-      P.b[buf][v][bt][1] = buf_load16(rb, ob + 16u);
-    }
-  }
+  for (int u = 0; u < 8; ++u)
+    if (active & (1u << u))
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(stage + 16 * (256 * u + 64 * wu)), 16,
+                                               (int)(doff[u] + ko), 0, 0, 0);
 }
 
-// Step st (wave-relative; ring slot SLOT, position S in its super-step).  Every load is
-// unconditional (indices past the range are clamped to the last step, a cache hit), so the
-// compiler can count outstanding loads exactly; scheduling barriers keep the prefetches
-// where they are issued.
+// s_waitcnt vmcnt(N) on gfx9: vmcnt in bits [3:0] and [15:14]; expcnt (bits [6:4]) and lgkmcnt
+// (bits [11:8]) at their maximum, i.e. not waited on.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | 0xF00 | ((N >> 4) << 14));
+}
+
+// Step st (wave-relative; ring slot and B stage SLOT, position S in its super-step).
+//   1. wait for this wave's loads of B(st) (the loads issued after them may stay in flight),
+//      then a barrier: B(st) of every wave is in LDS and every wave is done with B(st-1);
+//   2. issue B(st+1) into the other stage, then decode + MFMA, then issue the codes of st+2.
+// Every code load is unconditional (indices past the range are clamped to the last step, a
+// cache hit), so the compiler can count outstanding loads exactly.
 template <class F, int NT, int G, int SLOT, int S>
-__device__ __forceinline__ void step(Pipe<F, NT, G>& P, buf_rsrc rc, buf_rsrc rb,
-                                     const uint32_t* coff, const uint32_t* boff, int st, int n_it) {
-  constexpr int WB = Pipe<F, NT, G>::WB, NB = Pipe<F, NT, G>::NBATCH;
+__device__ __forceinline__ void step(Pipe<F, NT, G>& P, buf_rsrc rc, buf_rsrc rb, uint8_t* bs0,
+                                     uint8_t* bs1, const uint32_t* coff, const uint32_t* doff,
+                                     uint32_t active, int wu, const uint32_t* bread, int st, int n_it) {
+  // loads issued after B(st): the codes of step st+1 and, at a super-step start, the scales
+  constexpr int kAfter = kRT * (F::kStepCodeBytes > 16 ? 2 : 1) + (S == 0 ? kRT : 0);
+  wait_vmcnt<kAfter>();
+  __syncthreads();
+  if (st + 1 < n_it) dma_b<G>(rb, SLOT ? bs0 : bs1, doff, active, wu, st + 1);
+  __builtin_amdgcn_sched_barrier(0);
+  const uint8_t* bsrc = SLOT ? bs1 : bs0;
   typename F::Tab tab[kRT];
 #pragma unroll
   for (int t = 0; t < kRT; ++t) tab[t] = F::table(F::step_scale(P.sc[t], S));
 #pragma unroll
-  for (int wb = 0; wb < NB; ++wb) {
-    const int buf = NB == 1 ? SLOT : (wb & 1);  // static batch parity
-    if (wb + 1 < NB)
-      load_batch<F, NT, G>(P, buf ^ 1, rb, boff, st, wb + 1);
-    else
-      load_batch<F, NT, G>(P, buf ^ 1, rb, boff, min(st + 1, n_it - 1), 0);
-    __builtin_amdgcn_sched_barrier(0);
+  for (int o = 0; o < 8; ++o) {
+    u32x4 b[NT];
 #pragma unroll
-    for (int v = 0; v < WB; ++v) {
-      const int j = wb * WB + v;
+    for (int bt = 0; bt < NT; ++bt) b[bt] = *reinterpret_cast<const u32x4*>(bsrc + bread[bt * 8 + o]);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+    for (int t = 0; t < kRT; ++t) {
+      const u32x4 a = F::decode(P.cw[SLOT][t], tab[t], o);
 #pragma unroll
-        for (int t = 0; t < kRT; ++t) {
-          const u32x4 a = F::decode(P.cw[SLOT][t], tab[t], 2 * j + h);
-#pragma unroll
-          for (int bt = 0; bt < NT; ++bt) P.acc[t][bt] = mfma_16x16x32_bf16(a, P.b[buf][v][bt][h], P.acc[t][bt]);
-        }
-      }
+      for (int bt = 0; bt < NT; ++bt) P.acc[t][bt] = mfma_16x16x32_bf16(a, b[bt], P.acc[t][bt]);
     }
   }
   load_codes<F, NT, G>(P, SLOT, rc, coff, min(st + 2, n_it - 1));
@@ -188,18 +195,19 @@ __device__ __forceinline__ void step(Pipe<F, NT, G>& P, buf_rsrc rc, buf_rsrc rb
 // st0 + s is (st0 + s) % 2, which is static because G is even or the caller alternates.
 template <class F, int NT, int G, int SLOT0>
 __device__ __forceinline__ void superstep(Pipe<F, NT, G>& P, buf_rsrc rc, buf_rsrc rs, buf_rsrc rb,
-                                          const uint32_t* coff, const uint32_t* soff,
-                                          const uint32_t* boff, int c, int n_it) {
+                                          uint8_t* bs0, uint8_t* bs1, const uint32_t* coff,
+                                          const uint32_t* soff, const uint32_t* doff, uint32_t active,
+                                          int wu, const uint32_t* bread, int c, int n_it) {
   const int n_ss = n_it / G;
 #pragma unroll
   for (int t = 0; t < kRT; ++t) P.sc[t] = P.sc_next[t];
   load_scales<F, NT, G>(P, rs, soff, min(c + 1, n_ss - 1));
   __builtin_amdgcn_sched_barrier(0);
-  step<F, NT, G, SLOT0, 0>(P, rc, rb, coff, boff, G * c, n_it);
-  if constexpr (G >= 2) step<F, NT, G, SLOT0 ^ 1, 1>(P, rc, rb, coff, boff, G * c + 1, n_it);
+  step<F, NT, G, SLOT0, 0>(P, rc, rb, bs0, bs1, coff, doff, active, wu, bread, G * c, n_it);
+  if constexpr (G >= 2) step<F, NT, G, SLOT0 ^ 1, 1>(P, rc, rb, bs0, bs1, coff, doff, active, wu, bread, G * c + 1, n_it);
   if constexpr (G == 4) {
-    step<F, NT, G, SLOT0, 2>(P, rc, rb, coff, boff, G * c + 2, n_it);
-    step<F, NT, G, SLOT0 ^ 1, 3>(P, rc, rb, coff, boff, G * c + 3, n_it);
+    step<F, NT, G, SLOT0, 2>(P, rc, rb, bs0, bs1, coff, doff, active, wu, bread, G * c + 2, n_it);
+    step<F, NT, G, SLOT0 ^ 1, 3>(P, rc, rb, bs0, bs1, coff, doff, active, wu, bread, G * c + 3, n_it);
   }
 }
 
@@ -214,9 +222,10 @@ __device__ __forceinline__ void stream_task(const uint8_t* __restrict__ codes,
                                             int rows_per_expert, int K, int width, int ktop,
                                             const uint16_t* __restrict__ bsrc, uint32_t bsrc_bytes,
                                             const int32_t* __restrict__ perm, int blk_rb, int KS,
-                                            int r0, int nrows, void* __restrict__ out,
-                                            f32x4 (*red)[kRT][kWave]) {
+                                            int r0, int nrows, void* __restrict__ out, uint8_t* bs0,
+                                            uint8_t* bs1) {
   const int lane = wave_lane(), w = threadIdx.x / kWave;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   const int i16 = lane & 15, q = lane >> 4;
   const int kpart = w % KS, rb_i = blk_rb * (4 / KS) + w / KS;
   const int n_it = (K / 256) / KS;      // steps of this wave (a multiple of G)
@@ -234,40 +243,67 @@ __device__ __forceinline__ void stream_task(const uint8_t* __restrict__ codes,
     coff[t] = (uint32_t)row * cbr + F::code_bytes((uint32_t)(k0 + 64 * G * q));
     soff[t] = (uint32_t)row * sbr + F::scale_bytes((uint32_t)(k0 + 64 * G * q));
   }
-  uint32_t boff[NT];
+  // B stage: KS parts x 16*NT tokens x 32 chunks of 16 bytes; chunk c of token n sits at
+  // position c ^ (n & 7) of the token's 512 bytes.
+  const int per_part = NT * 16 * 32;    // chunks per K part
+  const int nrounds = KS * NT * 2;      // 256-chunk rounds of the workgroup (<= 8)
+  uint32_t doff[8];
 #pragma unroll
-  for (int bt = 0; bt < NT; ++bt) {
-    const int n = 16 * bt + i16;
-    boff[bt] = kOffNone;
-    if (n < nrows) {
-      const uint32_t rowb = FC == 1 ? (uint32_t)(perm[r0 + n] / ktop) : (uint32_t)(r0 + n);
-      boff[bt] = (rowb * (uint32_t)K + (uint32_t)k0 + 64u * G * q) * 2u;
-    }
+  for (int u = 0; u < 8; ++u) {
+    const int f = 256 * u + 64 * w + lane;
+    const int p = f / per_part, rem = f - p * per_part, n = rem >> 5, pos = rem & 31;
+    const int c = pos ^ (n & 7);
+    // unconditional (clamped) row lookups, so the eight loads issue together
+    const int nn = min(n, nrows - 1);
+    const uint32_t rowb = FC == 1 ? (uint32_t)(perm[r0 + nn] / ktop) : (uint32_t)(r0 + nn);
+    const uint32_t o = (rowb * (uint32_t)K + (uint32_t)(256 * n_it * p) + 64u * G * (uint32_t)(c >> 3)) * 2u +
+                       16u * (uint32_t)(c & 7);
+    doff[u] = (u < nrounds && n < nrows) ? o : kOffNone;
   }
+  // rounds of this wave that carry at least one real token row (a round of a wave covers the
+  // 2 token rows of its 64 chunks); the others are not issued
+  uint32_t active = 0;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int n_lo = ((256 * u + 64 * wu) % per_part) >> 5;
+    if (u < nrounds && n_lo < nrows) active |= 1u << u;
+  }
+  uint32_t bread[NT * 8];  // LDS byte offsets of this lane's B operands in a stage
+#pragma unroll
+  for (int bt = 0; bt < NT; ++bt)
+#pragma unroll
+    for (int o = 0; o < 8; ++o)
+      bread[bt * 8 + o] = (uint32_t)(kpart * per_part * 16 + (16 * bt + i16) * 512 + 16 * ((8 * q + o) ^ (i16 & 7)));
+
   Pipe<F, NT, G> P;
 #pragma unroll
   for (int t = 0; t < kRT; ++t)
 #pragma unroll
     for (int bt = 0; bt < NT; ++bt) P.acc[t][bt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // prologue: scales of super-step 0, codes of steps 0 and 1, token batch 0
+  // prologue: scales of super-step 0, codes of step 0, B of step 0, codes of step 1 (the order
+  // the per-step vmcnt accounting assumes)
   load_scales<F, NT, G>(P, rs, soff, 0);
   load_codes<F, NT, G>(P, 0, rc, coff, 0);
+  dma_b<G>(rb, bs0, doff, active, wu, 0);
   load_codes<F, NT, G>(P, 1, rc, coff, min(1, n_it - 1));
-  load_batch<F, NT, G>(P, 0, rb, boff, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
   const int n_ss = n_it / G;
   if constexpr (G == 1) {
     int c = 0;
     for (; c + 1 < n_ss; c += 2) {
-      superstep<F, NT, G, 0>(P, rc, rs, rb, coff, soff, boff, c, n_it);
-      superstep<F, NT, G, 1>(P, rc, rs, rb, coff, soff, boff, c + 1, n_it);
+      superstep<F, NT, G, 0>(P, rc, rs, rb, bs0, bs1, coff, soff, doff, active, wu, bread, c, n_it);
+      superstep<F, NT, G, 1>(P, rc, rs, rb, bs0, bs1, coff, soff, doff, active, wu, bread, c + 1, n_it);
     }
-    if (c < n_ss) superstep<F, NT, G, 0>(P, rc, rs, rb, coff, soff, boff, c, n_it);
+    if (c < n_ss) superstep<F, NT, G, 0>(P, rc, rs, rb, bs0, bs1, coff, soff, doff, active, wu, bread, c, n_it);
   } else {
-    for (int c = 0; c < n_ss; ++c) superstep<F, NT, G, 0>(P, rc, rs, rb, coff, soff, boff, c, n_it);
+    for (int c = 0; c < n_ss; ++c)
+      superstep<F, NT, G, 0>(P, rc, rs, rb, bs0, bs1, coff, soff, doff, active, wu, bread, c, n_it);
   }
 
   // Epilogue, one token tile at a time.  With KS > 1 the K parts of the waves that share a
-  // row block are summed through LDS in a fixed order.
+  // row block are summed through LDS (over the first B stage, free now) in a fixed order.
+  f32x4 (*red)[kRT][kWave] = reinterpret_cast<f32x4 (*)[kRT][kWave]>(bs0);
+  __syncthreads();  // every wave is done reading the B stages
 #pragma unroll
   for (int bt = 0; bt < NT; ++bt) {
     f32x4 v[kRT];
@@ -305,7 +341,7 @@ __device__ __forceinline__ void stream_task(const uint8_t* __restrict__ codes,
         for (int t = 0; t < kRT; ++t) *reinterpret_cast<f32x4*>(y + 16 * t) = v[t];
       }
     }
-    if (KS > 1) __syncthreads();
+    __syncthreads();  // the LDS of this tile / stage is reused by the next tile or task
   }
 }
 
@@ -316,7 +352,8 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int rows_per_expert,
     int K, int width, int ktop, const uint16_t* __restrict__ bsrc, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ plan, uint32_t bsrc_bytes, int KS, void* __restrict__ out) {
-  __shared__ f32x4 red[4][kRT][kWave];
+  __shared__ __align__(16) uint8_t bs0[kBStage];
+  __shared__ __align__(16) uint8_t bs1[kBStage];
   const int n_items = plan[0];
   const int4* items = reinterpret_cast<const int4*>(plan + 4);
   const int rb_per_item = FC == 1 ? width / 32 : rows_per_expert / 64;
@@ -329,10 +366,10 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(
     const int r0 = itm.y, nrows = itm.z;
     if (nrows <= 16)
       stream_task<F, FC, 1, G>(codes, scales, ebase, rows_per_expert, K, width, ktop, bsrc, bsrc_bytes,
-                               perm, grp, KS, r0, nrows, out, red);
+                               perm, grp, KS, r0, nrows, out, bs0, bs1);
     else
       stream_task<F, FC, 2, G>(codes, scales, ebase, rows_per_expert, K, width, ktop, bsrc, bsrc_bytes,
-                               perm, grp, KS, r0, nrows, out, red);
+                               perm, grp, KS, r0, nrows, out, bs0, bs1);
   }
 }
 
