@@ -10,9 +10,14 @@ routing) at T = 64 tokens.
 Every step is timed with HIP events on the stream the kernels run on; the last-level
 caches are flushed between steps (outside the events) by *reading* a 1 GiB buffer, so the
 expert weights come from HBM.  (A write flush would leave the 256 MB last-level cache full of
-dirty lines whose write-back then competes with the timed kernels: a measurement artefact.)  The FC1 kernel (2/3 of the weight bytes) is the dominant
-kernel: its algorithmic bytes (packed weights of the experts that received tokens, x read
-once, h written once) divided by its event-timed duration give `roofline.achieved`.
+dirty lines whose write-back then competes with the timed kernels: a measurement artefact.)
+Steps are timed twice: launched eagerly (each FFN stage between its own pair of events, which
+gives the per-kernel times), and as one HIP graph capturing the step, replayed -- the way a
+serving loop runs the decode step; `value` comes from the graph replays, checked to give the
+eager result bit for bit.  The FC1 kernel (2/3 of the weight bytes and flops) is the dominant
+kernel: its algorithmic bytes (decode: packed weights of the experts that received tokens, x
+read once, h written once) or flops (prefill) divided by its event-timed duration give
+`roofline.achieved`.
 
 Prints one JSON line.  `--gpus` above 1 is refused: this path runs on one GPU.
 """
@@ -182,9 +187,40 @@ def measure(sp: dict, dw, T: int, steps: int, warmup: int, flush_between: bool =
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # the same step captured once in a HIP graph and replayed (the decode step of a serving
+    # loop is graph-captured): no per-kernel launch gaps; caches flushed between replays too
+    graph_ms = None
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(warmup):
+            g.replay()
+        gev = [(ev(), ev()) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            if flush_between:
+                flush.sum()
+            gev[i][0].record(stream)
+            g.replay()
+            gev[i][1].record(stream)
+        torch.cuda.synchronize()
+        graph_ms = [a.elapsed_time(b) for a, b in gev]
+        # the replayed layer must produce the eager result
+        out_graph = out.clone()
+        step()
+        torch.cuda.synchronize()
+        if not torch.equal(out_graph, out):
+            raise RuntimeError("graph replay differs from the eager step")
+    except RuntimeError as e:  # capture unsupported: report the eager number only
+        print(f"[bench] graph replay skipped: {e}", file=sys.stderr, flush=True)
+        graph_ms = None
+
     step_ms = [e[0].elapsed_time(e[-1]) for e in all_evs]
     stage_ms = [[e[1 + 2 * s].elapsed_time(e[2 + 2 * s]) for e in all_evs] for s in range(n_stages)]
-    ms = float(np.mean(step_ms))
+    eager_ms = float(np.mean(step_ms))
+    ms = float(np.mean(graph_ms)) if graph_ms else eager_ms
     fc1_ms = float(np.mean(stage_ms[1]))
     fc2_ms = float(np.mean(stage_ms[2]))
     w1b = n_active * weight_bytes_per_expert(sp, 1)
@@ -225,12 +261,14 @@ def measure(sp: dict, dw, T: int, steps: int, warmup: int, flush_between: bool =
         "config": {"workload": workload, "tokens": T, "experts_active": n_active,
                    "cache_flush_between_steps": flush_between},
         "roofline": roof,
-        "stages_ms": {"route+permute+prepare+combine": ms - fc1_ms - fc2_ms, "fc1": fc1_ms, "fc2": fc2_ms},
+        "step_timing": "HIP graph replay" if graph_ms else "eager launches",
+        "ms_per_step_eager": eager_ms,
+        "stages_ms": {"route+permute+prepare+combine (eager)": eager_ms - fc1_ms - fc2_ms, "fc1": fc1_ms, "fc2": fc2_ms},
         "ffn_stage_ms": [float(np.mean(v)) for v in stage_ms],
         "weight_GBps_fc1_fc2": (w1b + w2b) / ((fc1_ms + fc2_ms) * 1e-3) / 1e9,
         "ffn_TFLOPs_fc1_fc2": all_flops / ((fc1_ms + fc2_ms) * 1e-3) / 1e12,
-        "ms_per_step_min": float(np.min(step_ms)),
-        "ms_per_step_median": float(np.median(step_ms)),
+        "ms_per_step_min": float(np.min(graph_ms or step_ms)),
+        "ms_per_step_median": float(np.median(graph_ms or step_ms)),
         "wall_s_timed_loop_incl_flush": wall,
     }
 
