@@ -21,17 +21,17 @@ inline moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE
 // Rows per work item of the streaming kernels: a group of one expert is split into items
 // of at most 32 rows (two 16-token MFMA tiles).
 constexpr int kStreamChunk = 32;
-// Batches of at least this many tokens run the grouped-GEMM kernels (prefill shape).
+// In batches of at least this many tokens, the groups larger than kStreamChunk rows run on the
+// grouped-GEMM kernels (items of kGemmRows rows); smaller groups always stream.
 constexpr int kGemmMinTokens = 128;
 
 // Hot experts are computed by the FP8 grouped GEMM on items of this many rows.
 constexpr int kHotChunk = 128;
 
 struct FfnLayout {
-  bool gemm;
-  int chunk;
-  int64_t max_items;
-  size_t plan_off, xp_off, h_off;
+  bool gemm;                    // the grouped-GEMM list is in use
+  int64_t max_items_s, max_items_g;
+  size_t plan_s_off, plan_g_off, xp_off, h_off;
   // hot experts (n_hot > 0)
   int64_t hot_max_items;
   size_t hot_plan_off, xq_off, xqs_off, hq_off, hqs_off, slots_off;
@@ -43,11 +43,14 @@ FfnLayout ffn_layout(const moe_weights* w, int T, int k) {
   FfnLayout L;
   const int64_t R = (int64_t)T * k;
   L.gemm = T >= kGemmMinTokens;
-  L.chunk = L.gemm ? kGemmRows : kStreamChunk;
-  L.max_items = (R + L.chunk - 1) / L.chunk + (R < w->E ? R : w->E);
+  const int64_t per_expert = R < w->E ? R : w->E;  // one partial item per expert at most
+  L.max_items_s = (R + kStreamChunk - 1) / kStreamChunk + per_expert;
+  L.max_items_g = L.gemm ? (R + kGemmRows - 1) / kGemmRows + per_expert : 0;
   size_t off = 0;
-  L.plan_off = off;
-  off = align256(off + plan_bytes(L.max_items));
+  L.plan_s_off = off;
+  off = align256(off + plan_bytes(L.max_items_s));
+  L.plan_g_off = off;
+  off = align256(off + plan_bytes(L.max_items_g));
   L.xp_off = off;  // x in k-slot order, T rows
   off = align256(off + (size_t)T * w->H * 2);
   L.h_off = off;  // h (bf16, k-slot order), R rows
@@ -189,10 +192,12 @@ moe_status ffn_check(const moe_weights* w, const uint16_t* x, int32_t T, int32_t
   return MOE_OK;
 }
 
-// Stages: 0 prepare (low-bit work list, x in k-slot order), 1 low-bit FC1 + SwiGLU, 2 low-bit
-// FC2; with a hot set, 3 hot prepare (hot work list, MXFP8 of x), then per batch of S hot
-// experts: convert into the slots, FP8 FC1 + SwiGLU + MXFP8 of h, FP8 FC2.
-constexpr int kLowbitStages = 3;
+// Stages: 0 prepare (low-bit work lists, x in k-slot order), 1 low-bit FC1 + SwiGLU on the
+// streaming list, 2 the same on the grouped-GEMM list, 3 low-bit FC2 streaming, 4 FC2 grouped
+// GEMM (stages 2 and 4 launch nothing below kGemmMinTokens tokens); with a hot set, 5 hot
+// prepare (hot work list, MXFP8 of x), then per batch of S hot experts: convert into the
+// slots, FP8 FC1 + SwiGLU + MXFP8 of h, FP8 FC2.
+constexpr int kLowbitStages = 5;
 
 int ffn_num_stages(const moe_weights* w, int T, int k, size_t ws_bytes) {
   if (w->n_hot <= 0) return kLowbitStages;
@@ -206,24 +211,30 @@ moe_status ffn_run_stage(const moe_weights* w, const uint16_t* x, int32_t T, int
                          float* y_perm, void* ws, size_t ws_bytes, int stage, hipStream_t s) {
   const FfnLayout L = ffn_layout(w, T, k);
   char* base = static_cast<char*>(ws);
-  int32_t* plan = reinterpret_cast<int32_t*>(base + L.plan_off);
+  int32_t* plan_s = reinterpret_cast<int32_t*>(base + L.plan_s_off);
+  int32_t* plan_g = reinterpret_cast<int32_t*>(base + L.plan_g_off);
   uint16_t* xp = reinterpret_cast<uint16_t*>(base + L.xp_off);
   uint16_t* hbuf = reinterpret_cast<uint16_t*>(base + L.h_off);
   const LowbitWeights lw = lowbit(w);
   hipError_t e = hipSuccess;
   switch (stage) {
     case 0:
-      e = launch_prepare(offsets, w->E, L.chunk, w->hot_ids, w->n_hot, false, plan, x, T, w->H, lw.fmt, xp, s);
+      e = launch_prepare(offsets, w->E, kStreamChunk, kGemmRows, L.gemm, w->hot_ids, w->n_hot, plan_s, plan_g,
+                         x, T, w->H, lw.fmt, xp, s);
       break;
     case 1:
-      e = L.gemm ? launch_lowbit_gemm_fc1(lw, w->H, w->I, k, xp, perm, plan, (int)L.max_items, T, hbuf, s)
-                 : launch_lowbit_fc1(lw, w->E, w->H, w->I, k, xp, perm, plan, (int)L.max_items, T, hbuf, s);
+      e = launch_lowbit_fc1(lw, w->E, w->H, w->I, k, xp, perm, plan_s, (int)L.max_items_s, T, hbuf, s);
       break;
     case 2:
-      e = L.gemm ? launch_lowbit_gemm_fc2(lw, w->H, w->I, k, hbuf, plan, (int)L.max_items, T, y_perm, s)
-                 : launch_lowbit_fc2(lw, w->E, w->H, w->I, k, hbuf, plan, (int)L.max_items, T, y_perm, s);
+      if (L.gemm) e = launch_lowbit_gemm_fc1(lw, w->H, w->I, k, xp, perm, plan_g, (int)L.max_items_g, T, hbuf, s);
       break;
     case 3:
+      e = launch_lowbit_fc2(lw, w->E, w->H, w->I, k, hbuf, plan_s, (int)L.max_items_s, T, y_perm, s);
+      break;
+    case 4:
+      if (L.gemm) e = launch_lowbit_gemm_fc2(lw, w->H, w->I, k, hbuf, plan_g, (int)L.max_items_g, T, y_perm, s);
+      break;
+    case 5:
       e = launch_hot_prepare(offsets, w->E, kHotChunk, w->hot_ids, w->n_hot,
                              reinterpret_cast<int32_t*>(base + L.hot_plan_off), x, T, w->H,
                              reinterpret_cast<uint8_t*>(base + L.xq_off),
@@ -231,7 +242,7 @@ moe_status ffn_run_stage(const moe_weights* w, const uint16_t* x, int32_t T, int
       break;
     default: {
       const int S = ffn_slots(w, L, ws_bytes);
-      const int b0 = ((stage - 4) / 3) * S, part = (stage - 4) % 3;
+      const int b0 = ((stage - kLowbitStages - 1) / 3) * S, part = (stage - kLowbitStages - 1) % 3;
       const int32_t* hplan = reinterpret_cast<const int32_t*>(base + L.hot_plan_off);
       uint8_t* slots = reinterpret_cast<uint8_t*>(base + L.slots_off);
       uint8_t* hq = reinterpret_cast<uint8_t*>(base + L.hq_off);

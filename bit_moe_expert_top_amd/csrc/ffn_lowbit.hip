@@ -23,16 +23,17 @@ namespace bitmoe {
 // ------------------------------------------------------------------ work list
 size_t plan_bytes(int64_t max_items) { return (size_t)(16 + 16 * max_items); }
 
-// Block 0 builds the work list; blocks 1.. store x in the k-slot order of the weight format.
-//   work list: plan[0] = number of items, then int4 items {expert, first row, rows, hot slot}:
-//   the grouped rows of every expert (low-bit experts, or hot experts if want_hot), split
-//   into items of at most `chunk` rows, experts in id order.
+// Block 0 builds the work lists; blocks 1.. store x in the k-slot order of the weight format.
+//   work lists (build_plan2): the grouped rows of every low-bit expert, in items of at most
+//   `small_max` rows for the streaming kernel, or (gemm_enabled, groups above small_max) of at
+//   most `gemm_chunk` rows for the grouped GEMM; experts in id order.
 //   2-bit: xp[t][16c + p] = x[t][16c + 4*(p%4) + p/4], one thread per 16 k (byte selects);
 //   3-bit: xp[t][32c + s] = x[t][32c + slot_k(s)], one thread per 32 k.
 __global__ __launch_bounds__(1024) void prepare_kernel(const int32_t* __restrict__ offsets, int E,
-                                                       int chunk, const int32_t* __restrict__ hot_ids,
-                                                       int n_hot, int want_hot,
-                                                       int32_t* __restrict__ plan,
+                                                       int small_max, int gemm_chunk, int gemm_enabled,
+                                                       const int32_t* __restrict__ hot_ids, int n_hot,
+                                                       int32_t* __restrict__ plan_s,
+                                                       int32_t* __restrict__ plan_g,
                                                        const uint4* __restrict__ x, int nchunks,
                                                        int fmt, uint4* __restrict__ xp) {
   if (blockIdx.x > 0) {
@@ -74,17 +75,17 @@ __global__ __launch_bounds__(1024) void prepare_kernel(const int32_t* __restrict
     }
     return;
   }
-  build_plan(offsets, E, chunk, hot_ids, n_hot, want_hot, plan);
+  build_plan2(offsets, E, small_max, gemm_chunk, gemm_enabled, hot_ids, n_hot, plan_s, plan_g);
 }
 
-hipError_t launch_prepare(const int32_t* offsets, int E, int chunk_rows, const int32_t* hot_ids,
-                          int n_hot, bool want_hot, int32_t* plan, const uint16_t* x, int T, int H,
-                          int fmt, uint16_t* xp, hipStream_t s) {
+hipError_t launch_prepare(const int32_t* offsets, int E, int small_max, int gemm_chunk, bool gemm_enabled,
+                          const int32_t* hot_ids, int n_hot, int32_t* plan_s, int32_t* plan_g,
+                          const uint16_t* x, int T, int H, int fmt, uint16_t* xp, hipStream_t s) {
   const int per = fmt == W2Fmt::kId ? 16 : 32;  // k per thread
   const int nchunks = xp ? T * (H / per) : 0;
   const int blocks = 1 + (nchunks + 1023) / 1024;
-  prepare_kernel<<<blocks, 1024, 0, s>>>(offsets, E, chunk_rows, hot_ids, n_hot, want_hot ? 1 : 0,
-                                         plan, (const uint4*)x, nchunks, fmt, (uint4*)xp);
+  prepare_kernel<<<blocks, 1024, 0, s>>>(offsets, E, small_max, gemm_chunk, gemm_enabled ? 1 : 0, hot_ids,
+                                         n_hot, plan_s, plan_g, (const uint4*)x, nchunks, fmt, (uint4*)xp);
   return hipGetLastError();
 }
 

@@ -33,13 +33,14 @@ struct LowbitWeights {
 };
 
 // Work list of grouped-row chunks built on the device from `offsets`.
-//   int32 header[4]: [0] = number of chunks; then int4 items {expert, first row, rows, 0}.
+//   int32 header[4]: [0] = number of items; then int4 items {expert, first row, rows, hot slot}.
 size_t plan_bytes(int64_t max_items);
-// One launch: the work list, and (if xp) x stored in the k-slot order of the weight format
-// `fmt` (1 = 2-bit, 2 = 3-bit).
-hipError_t launch_prepare(const int32_t* offsets, int E, int chunk_rows, const int32_t* hot_ids,
-                          int n_hot, bool want_hot, int32_t* plan, const uint16_t* x, int T, int H,
-                          int fmt, uint16_t* xp, hipStream_t s);
+// One launch: the two low-bit work lists (streaming items of <= small_max rows; grouped-GEMM
+// items of <= gemm_chunk rows for experts above small_max if gemm_enabled), and (if xp) x
+// stored in the k-slot order of the weight format `fmt` (1 = 2-bit, 2 = 3-bit).
+hipError_t launch_prepare(const int32_t* offsets, int E, int small_max, int gemm_chunk, bool gemm_enabled,
+                          const int32_t* hot_ids, int n_hot, int32_t* plan_s, int32_t* plan_g,
+                          const uint16_t* x, int T, int H, int fmt, uint16_t* xp, hipStream_t s);
 
 // Decode-style kernels: weight-streaming, MFMA on 16-token tiles.
 hipError_t launch_lowbit_fc1(const LowbitWeights& w, int E, int H, int I, int k,

@@ -144,10 +144,12 @@ moe_status moe_expert_ffn(const moe_weights* w, const uint16_t* x, int32_t T, in
  * n = moe_expert_ffn_num_stages(w, T, k, ws_bytes), in order on one stream with the same
  * arguments and workspace is exactly moe_expert_ffn.  Each stage is a single kernel launch, so
  * a caller can time the kernels one by one (HIP events on `stream`) or interleave other work.
- * Stages: 0 = low-bit work list and x in the MFMA k-slot order, 1 = low-bit FC1 + SwiGLU,
- * 2 = low-bit FC2.  With a hot set (n_hot > 0): 3 = hot work list and MXFP8 of x, then for
- * each batch of S hot experts (S = FP8 slots in the workspace): convert the batch's hot
- * experts that have rows into the slots, FP8 FC1 + SwiGLU + MXFP8 of h, FP8 FC2.
+ * Stages: 0 = low-bit work lists and x in the MFMA k-slot order; 1 = low-bit FC1 + SwiGLU of
+ * the groups of <= 32 rows (weight-streaming kernel); 2 = the same for larger groups (grouped
+ * GEMM, batches of >= 128 tokens; launches nothing below); 3, 4 = FC2 likewise.  With a hot
+ * set (n_hot > 0): 5 = hot work list and MXFP8 of x, then for each batch of S hot experts
+ * (S = FP8 slots in the workspace): convert the batch's hot experts that have rows into the
+ * slots, FP8 FC1 + SwiGLU + MXFP8 of h, FP8 FC2.
  * num_stages returns 0 for invalid arguments or T = 0.
  * Errors: as moe_expert_ffn; INVALID_ARG for a stage out of range. */
 int32_t moe_expert_ffn_num_stages(const moe_weights* w, int32_t T, int32_t k, size_t ws_bytes);
