@@ -17,6 +17,8 @@
 //       I + 64n + 32wn + [0,32) as its two MFMA column tiles, so gate and up of one h column
 //       sit in the same lane and SwiGLU is applied in the epilogue (h stored bf16).
 //   FC2 column tile n: weight rows 128n + [0,128); the epilogue stores y (fp32).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "lowbit_fmt.h"
@@ -91,35 +93,39 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(
     const uint32_t soff = (uint32_t)wrow * sbr + (F::kId == W2Fmt::kId ? 2u * hsel : 0u);
     const uint32_t cstep = F::code_bytes(kBK), sstep = F::scale_bytes(kBK);
 
-    // register staging of one K step
-    u32x4 areg[4];
-    uint32_t creg[F::kFieldWords];
-    uint32_t sreg;
-    auto load_step = [&](int kb) {
+    // register staging of K steps, two deep: the loads of step kb + 2 are issued while step kb
+    // is computed from LDS and step kb + 1 waits in registers to be stored
+    struct Staged {
+      u32x4 a[4];
+      uint32_t c[F::kFieldWords];
+      uint32_t s;
+    };
+    Staged stg[2];
+    auto load_step = [&](Staged& g, int kb) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) areg[u] = buf_load16(ra, aoff[u] + (uint32_t)kb * kBK * 2u);
+      for (int u = 0; u < 4; ++u) g.a[u] = buf_load16(ra, aoff[u] + (uint32_t)kb * kBK * 2u);
       const uint32_t co = coff + (uint32_t)kb * cstep, so = soff + (uint32_t)kb * sstep;
       const uint64_t c01 = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rc, (int)co, 0, 0));
-      creg[0] = (uint32_t)c01;
-      creg[1] = (uint32_t)(c01 >> 32);
-      if constexpr (F::kFieldWords == 3) creg[2] = buf_load4(rc, co + 8u);
+      g.c[0] = (uint32_t)c01;
+      g.c[1] = (uint32_t)(c01 >> 32);
+      if constexpr (F::kFieldWords == 3) g.c[2] = buf_load4(rc, co + 8u);
       if constexpr (F::kId == W2Fmt::kId)
-        sreg = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, (int)so, 0, 0);
+        g.s = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, (int)so, 0, 0);
       else
-        sreg = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, (int)so, 0, 0);
+        g.s = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, (int)so, 0, 0);
     };
-    auto store_step = [&](int buf) {
+    auto store_step = [&](const Staged& g, int buf) {
       uint16_t* la = lds + buf * 2 * kTileElems;
       uint16_t* lbm = la + kTileElems;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int r = (tid >> 3) + 32 * u;
-        *reinterpret_cast<u32x4*>(la + r * kLdsRow + 8 * (tid & 7)) = areg[u];
+        *reinterpret_cast<u32x4*>(la + r * kLdsRow + 8 * (tid & 7)) = g.a[u];
       }
-      const typename F::Tab tab = F::table32(sreg);
+      const typename F::Tab tab = F::table32(g.s);
       uint16_t* dst = lbm + j * kLdsRow + 32 * hsel;
 #pragma unroll
-      for (int op = 0; op < 4; ++op) *reinterpret_cast<u32x4*>(dst + 8 * op) = F::decode32(creg, tab, op);
+      for (int op = 0; op < 4; ++op) *reinterpret_cast<u32x4*>(dst + 8 * op) = F::decode32(g.c, tab, op);
     };
 
     f32x16 acc[2][2];
@@ -130,13 +136,13 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
 
-    load_step(0);
-    store_step(0);
-    __syncthreads();
-    for (int kb = 0; kb < nk; ++kb) {
-      const int buf = kb & 1;
-      load_step(min(kb + 1, nk - 1));  // unconditional (the last step reloads itself)
-      const uint16_t* la = lds + buf * 2 * kTileElems;
+    // one K step from LDS buffer P; staging slot P is refilled with step kb + 2 and slot P^1
+    // (step kb + 1) is stored into the other LDS buffer.  Loads are unconditional (clamped).
+    auto iter = [&](auto P_, int kb) {
+      constexpr int P = decltype(P_)::value;
+      load_step(stg[P], min(kb + 2, nk - 1));
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this step's LDS reads
+      const uint16_t* la = lds + P * 2 * kTileElems;
       const uint16_t* lbm = la + kTileElems;
 #pragma unroll
       for (int kk = 0; kk < kBK / 16; ++kk) {
@@ -152,8 +158,17 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(
 #pragma unroll
           for (int b = 0; b < 2; ++b) acc[a][b] = mfma_32x32x16_bf16(av[a], bv[b], acc[a][b]);
       }
-      if (kb + 1 < nk) store_step(buf ^ 1);
+      if (kb + 1 < nk) store_step(stg[P ^ 1], P ^ 1);
       __syncthreads();
+    };
+
+    load_step(stg[0], 0);
+    load_step(stg[1], min(1, nk - 1));
+    store_step(stg[0], 0);
+    __syncthreads();
+    for (int kb = 0; kb < nk; kb += 2) {  // nk is even (K is a multiple of 256)
+      iter(std::integral_constant<int, 0>{}, kb);
+      iter(std::integral_constant<int, 1>{}, kb + 1);
     }
 
     // ---- epilogue
