@@ -93,11 +93,14 @@ hipError_t launch_prepare(const int32_t* offsets, int E, int small_max, int gemm
 
 constexpr int kRT = 4;  // 16-row A tiles per wave (64 weight rows)
 
-// Lane -> k mapping.  A wave walks its K range in super-steps of G 64-k steps per quad.  In
-// super-step c, step s (0 <= s < G), the lanes of quad q handle the 64 consecutive k
+// Lane -> k mapping.  A wave walks its K range in super-steps of G (1 or 2) 64-k steps per
+// quad.  In super-step c, step s (0 <= s < G), the lanes of quad q handle the 64 consecutive k
 //     kbase + 256*G*c + 64*G*q + 64*s + [0, 64)
-// so over a super-step a lane covers 64*G consecutive k: its scales for the whole super-step
-// are contiguous bytes (one load), and its codes for step s are contiguous (one or two loads).
+// so over a super-step a lane covers 64*G consecutive k and the four quads of a row 256*G
+// consecutive k: with G = 2 and 2-bit codes that is one whole 128-byte line per row, requested
+// by one group of loads issued together (lines split over loads issued far apart were evicted
+// from the L2 between their uses and fetched again).  A lane's scales for the super-step are
+// contiguous bytes (one load).
 //
 // The token operand (B) of a step is staged in LDS once per workgroup and shared by its 4
 // waves: direct global -> LDS loads (16 bytes per lane, no registers), double buffered, one
@@ -107,23 +110,25 @@ constexpr int kRT = 4;  // 16-row A tiles per wave (64 weight rows)
 constexpr int kBStage = 4 * 16 * 512;  // the largest stage: KS = 4 x 16 tokens (or KS = 1 x 32)
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Per-wave pipeline state: the codes of steps in a two-slot ring (issued two steps ahead), the
-// scales of the current and the next super-step, and the accumulators.
+// Per-wave pipeline state: the codes of two super-steps (the current one and the next, issued
+// one super-step ahead), the scales of the current and the next super-step, the accumulators.
 template <class F, int NT, int G>
 struct Pipe {
   static constexpr int SB = F::kStepScaleBytes * G;
-  typename F::Codes cw[2][kRT];
+  typename F::Codes cw[2][G][kRT];
   ScaleBytes<SB> sc[kRT], sc_next[kRT];
   f32x4 acc[kRT][NT];
 };
 
-// Loads of step `st` (wave-relative) into ring slot `slot`.
+// Codes of super-step c (all G steps, issued together) into ring slot `slot`.
 template <class F, int NT, int G>
 __device__ __forceinline__ void load_codes(Pipe<F, NT, G>& P, int slot, buf_rsrc rc,
-                                           const uint32_t* coff, int st) {
-  const uint32_t o = F::code_bytes(256u * G * (uint32_t)(st / G) + 64u * (uint32_t)(st % G));
+                                           const uint32_t* coff, int c) {
 #pragma unroll
-  for (int t = 0; t < kRT; ++t) P.cw[slot][t] = F::load_codes(rc, coff[t] + o);
+  for (int t = 0; t < kRT; ++t)
+#pragma unroll
+    for (int s = 0; s < G; ++s)
+      P.cw[slot][s][t] = F::load_codes(rc, coff[t] + F::code_bytes(256u * G * (uint32_t)c + 64u * (uint32_t)s));
 }
 
 template <class F, int NT, int G>
@@ -156,23 +161,32 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | 0xF00 | ((N >> 4) << 14));
 }
 
-// Step st (wave-relative; ring slot and B stage SLOT, position S in its super-step).
-//   1. wait for this wave's loads of B(st) (the loads issued after them may stay in flight),
-//      then a barrier: B(st) of every wave is in LDS and every wave is done with B(st-1);
-//   2. issue B(st+1) into the other stage, then decode + MFMA, then issue the codes of st+2.
-// Every code load is unconditional (indices past the range are clamped to the last step, a
-// cache hit), so the compiler can count outstanding loads exactly.
-template <class F, int NT, int G, int SLOT, int S>
-__device__ __forceinline__ void step(Pipe<F, NT, G>& P, buf_rsrc rc, buf_rsrc rb, uint8_t* bs0,
-                                     uint8_t* bs1, const uint32_t* coff, const uint32_t* doff,
-                                     uint32_t active, int wu, const uint32_t* bread, int st, int n_it) {
-  // loads issued after B(st): the codes of step st+1 and, at a super-step start, the scales
-  constexpr int kAfter = kRT * (F::kStepCodeBytes > 16 ? 2 : 1) + (S == 0 ? kRT : 0);
+// Step st = G*c + S of super-step c (code ring slot CS, B stage BS = st % 2).
+//   1. wait for this wave's loads of B(st) -- vector loads complete in issue order, so at S = 1
+//      the next super-step's codes and scales (issued after B(st)) may stay in flight -- then
+//      a barrier: B(st) of every wave is in LDS and every wave is done with B(st-1);
+//   2. issue B(st+1) into the other stage; at S = 0 then issue the codes and scales of
+//      super-step c+1; decode + MFMA.
+template <class F, int NT, int G, int CS, int BS, int S>
+__device__ __forceinline__ void step(Pipe<F, NT, G>& P, buf_rsrc rc, buf_rsrc rs, buf_rsrc rb, uint8_t* bs0,
+                                     uint8_t* bs1, const uint32_t* coff, const uint32_t* soff,
+                                     const uint32_t* doff, uint32_t active, int wu, const uint32_t* bread,
+                                     int c, int n_it) {
+  constexpr int kLc = F::kStepCodeBytes > 16 ? 2 : 1;  // load instructions per tile and step
+  constexpr int kAfter = S == 1 ? kRT * (1 + G * kLc) : 0;
+  const int st = G * c + S;
   wait_vmcnt<kAfter>();
   __syncthreads();
-  if (st + 1 < n_it) dma_b<G>(rb, SLOT ? bs0 : bs1, doff, active, wu, st + 1);
+  if (st + 1 < n_it) dma_b<G>(rb, BS ? bs0 : bs1, doff, active, wu, st + 1);
+  if constexpr (S == 0) {
+    const int n_ss = n_it / G;
+#pragma unroll
+    for (int t = 0; t < kRT; ++t) P.sc[t] = P.sc_next[t];
+    load_scales<F, NT, G>(P, rs, soff, min(c + 1, n_ss - 1));
+    load_codes<F, NT, G>(P, CS ^ 1, rc, coff, min(c + 1, n_ss - 1));
+  }
   __builtin_amdgcn_sched_barrier(0);
-  const uint8_t* bsrc = SLOT ? bs1 : bs0;
+  const uint8_t* bsrc = BS ? bs1 : bs0;
   typename F::Tab tab[kRT];
 #pragma unroll
   for (int t = 0; t < kRT; ++t) tab[t] = F::table(F::step_scale(P.sc[t], S));
@@ -183,33 +197,24 @@ __device__ __forceinline__ void step(Pipe<F, NT, G>& P, buf_rsrc rc, buf_rsrc rb
     for (int bt = 0; bt < NT; ++bt) b[bt] = *reinterpret_cast<const u32x4*>(bsrc + bread[bt * 8 + o]);
 #pragma unroll
     for (int t = 0; t < kRT; ++t) {
-      const u32x4 a = F::decode(P.cw[SLOT][t], tab[t], o);
+      const u32x4 a = F::decode(P.cw[CS][S][t], tab[t], o);
 #pragma unroll
       for (int bt = 0; bt < NT; ++bt) P.acc[t][bt] = mfma_16x16x32_bf16(a, b[bt], P.acc[t][bt]);
     }
   }
-  load_codes<F, NT, G>(P, SLOT, rc, coff, min(st + 2, n_it - 1));
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// One super-step (G steps) starting at wave-relative step st0 = G*c; the ring slot of step
-// st0 + s is (st0 + s) % 2, which is static because G is even or the caller alternates.
-template <class F, int NT, int G, int SLOT0>
+// One super-step c (code ring slot CS = c % 2).
+template <class F, int NT, int G, int CS>
 __device__ __forceinline__ void superstep(Pipe<F, NT, G>& P, buf_rsrc rc, buf_rsrc rs, buf_rsrc rb,
                                           uint8_t* bs0, uint8_t* bs1, const uint32_t* coff,
                                           const uint32_t* soff, const uint32_t* doff, uint32_t active,
                                           int wu, const uint32_t* bread, int c, int n_it) {
-  const int n_ss = n_it / G;
-#pragma unroll
-  for (int t = 0; t < kRT; ++t) P.sc[t] = P.sc_next[t];
-  load_scales<F, NT, G>(P, rs, soff, min(c + 1, n_ss - 1));
-  __builtin_amdgcn_sched_barrier(0);
-  step<F, NT, G, SLOT0, 0>(P, rc, rb, bs0, bs1, coff, doff, active, wu, bread, G * c, n_it);
-  if constexpr (G >= 2) step<F, NT, G, SLOT0 ^ 1, 1>(P, rc, rb, bs0, bs1, coff, doff, active, wu, bread, G * c + 1, n_it);
-  if constexpr (G == 4) {
-    step<F, NT, G, SLOT0, 2>(P, rc, rb, bs0, bs1, coff, doff, active, wu, bread, G * c + 2, n_it);
-    step<F, NT, G, SLOT0 ^ 1, 3>(P, rc, rb, bs0, bs1, coff, doff, active, wu, bread, G * c + 3, n_it);
-  }
+  // B stage of step G*c + S is its parity: S for G = 2, CS for G = 1
+  step<F, NT, G, CS, (G == 1 ? CS : 0), 0>(P, rc, rs, rb, bs0, bs1, coff, soff, doff, active, wu, bread, c, n_it);
+  if constexpr (G == 2)
+    step<F, NT, G, CS, 1, 1>(P, rc, rs, rb, bs0, bs1, coff, soff, doff, active, wu, bread, c, n_it);
 }
 
 // One wave's task: 64 weight rows (4 A tiles) x a K range, for the NT*16 tokens of one item.
@@ -281,25 +286,18 @@ __device__ __forceinline__ void stream_task(const uint8_t* __restrict__ codes,
   for (int t = 0; t < kRT; ++t)
 #pragma unroll
     for (int bt = 0; bt < NT; ++bt) P.acc[t][bt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // prologue: scales of super-step 0, codes of step 0, B of step 0, codes of step 1 (the order
-  // the per-step vmcnt accounting assumes)
+  // prologue: scales and codes of super-step 0, B of step 0
   load_scales<F, NT, G>(P, rs, soff, 0);
   load_codes<F, NT, G>(P, 0, rc, coff, 0);
   dma_b<G>(rb, bs0, doff, active, wu, 0);
-  load_codes<F, NT, G>(P, 1, rc, coff, min(1, n_it - 1));
   __builtin_amdgcn_sched_barrier(0);
   const int n_ss = n_it / G;
-  if constexpr (G == 1) {
-    int c = 0;
-    for (; c + 1 < n_ss; c += 2) {
-      superstep<F, NT, G, 0>(P, rc, rs, rb, bs0, bs1, coff, soff, doff, active, wu, bread, c, n_it);
-      superstep<F, NT, G, 1>(P, rc, rs, rb, bs0, bs1, coff, soff, doff, active, wu, bread, c + 1, n_it);
-    }
-    if (c < n_ss) superstep<F, NT, G, 0>(P, rc, rs, rb, bs0, bs1, coff, soff, doff, active, wu, bread, c, n_it);
-  } else {
-    for (int c = 0; c < n_ss; ++c)
-      superstep<F, NT, G, 0>(P, rc, rs, rb, bs0, bs1, coff, soff, doff, active, wu, bread, c, n_it);
+  int c = 0;
+  for (; c + 1 < n_ss; c += 2) {
+    superstep<F, NT, G, 0>(P, rc, rs, rb, bs0, bs1, coff, soff, doff, active, wu, bread, c, n_it);
+    superstep<F, NT, G, 1>(P, rc, rs, rb, bs0, bs1, coff, soff, doff, active, wu, bread, c + 1, n_it);
   }
+  if (c < n_ss) superstep<F, NT, G, 0>(P, rc, rs, rb, bs0, bs1, coff, soff, doff, active, wu, bread, c, n_it);
 
   // Epilogue, one token tile at a time.  With KS > 1 the K parts of the waves that share a
   // row block are summed through LDS (over the first B stage, free now) in a fixed order.
@@ -388,10 +386,10 @@ static int k_split_for(int T, int K) {
   return ks;
 }
 
-// Super-step length: the largest of 4, 2, 1 dividing the steps of a wave.
+// Super-step length: 2 steps when the steps of a wave are even, else 1.
 static int super_step_for(int K, int ks) {
   const int n = (K / 256) / ks;
-  return n % 4 == 0 ? 4 : (n % 2 == 0 ? 2 : 1);
+  return n % 2 == 0 ? 2 : 1;
 }
 
 template <class F, int FC>
@@ -402,9 +400,7 @@ static hipError_t launch_stream(const void* codes, const void* scales, int rows,
   const int g = super_step_for(K, ks), grid = grid_for(tasks);
   const uint8_t* c = (const uint8_t*)codes;
   const uint8_t* sc = (const uint8_t*)scales;
-  if (g == 4)
-    stream_kernel<F, FC, 4><<<grid, 256, 0, s>>>(c, sc, rows, K, width, ktop, bsrc, perm, plan, bsrc_bytes, ks, out);
-  else if (g == 2)
+  if (g == 2)
     stream_kernel<F, FC, 2><<<grid, 256, 0, s>>>(c, sc, rows, K, width, ktop, bsrc, perm, plan, bsrc_bytes, ks, out);
   else
     stream_kernel<F, FC, 1><<<grid, 256, 0, s>>>(c, sc, rows, K, width, ktop, bsrc, perm, plan, bsrc_bytes, ks, out);
