@@ -15,6 +15,8 @@
 // half h = l / 32) holds k = 32c + 16h + [0,16) in chunk c, and its scale operand is the
 // e8m0 scale of the 32-k block h.  (Established on the device: data and scales placed this
 // way reproduce the fp64 product of the dequantised operands.)
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "mx_fmt.h"
@@ -230,18 +232,23 @@ __global__ __launch_bounds__(256, 2) void fp8_gemm_kernel(
     for (int u = 0; u < 4; ++u) boff[u] = (uint32_t)wrow_of((tid >> 3) + 32 * u) * K + 16u * (tid & 7);
     const uint32_t bsoff = tid >= 128 ? (uint32_t)wrow_of(tid - 128) * kb32 : kOffNone;
 
-    u32x4 areg[4], breg[4];
-    uint32_t sreg;
-    auto load_step = [&](int kb) {
+    // register staging of K steps, two deep: the loads of step kb + 2 are issued before step kb
+    // is computed from LDS; step kb + 1 waits in registers and is stored after the MFMAs
+    struct Staged {
+      u32x4 a[4], b[4];
+      uint32_t s;
+    };
+    Staged stg[2];
+    auto load_step = [&](Staged& g, int kb) {
       const uint32_t ko = (uint32_t)kb * kF8BK;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        areg[u] = buf_load16(ra, aoff[u] + ko);
-        breg[u] = buf_load16(rb, boff[u] + ko);
+        g.a[u] = buf_load16(ra, aoff[u] + ko);
+        g.b[u] = buf_load16(rb, boff[u] + ko);
       }
-      sreg = tid < 128 ? buf_load4(ras, asoff + 4u * kb) : buf_load4(rbs, bsoff + 4u * kb);
+      g.s = tid < 128 ? buf_load4(ras, asoff + 4u * kb) : buf_load4(rbs, bsoff + 4u * kb);
     };
-    auto store_step = [&](int buf) {
+    auto store_step = [&](const Staged& g, int buf) {
       uint8_t* la = lds8 + buf * kF8Buf;
       uint8_t* lb = la + kF8Tile;
       uint8_t* lsa = lb + kF8Tile;
@@ -249,11 +256,11 @@ __global__ __launch_bounds__(256, 2) void fp8_gemm_kernel(
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int r = (tid >> 3) + 32 * u;
-        *reinterpret_cast<u32x4*>(la + r * kF8Row + 16 * (tid & 7)) = areg[u];
-        *reinterpret_cast<u32x4*>(lb + r * kF8Row + 16 * (tid & 7)) = breg[u];
+        *reinterpret_cast<u32x4*>(la + r * kF8Row + 16 * (tid & 7)) = g.a[u];
+        *reinterpret_cast<u32x4*>(lb + r * kF8Row + 16 * (tid & 7)) = g.b[u];
       }
-      if (tid < 128) *reinterpret_cast<uint32_t*>(lsa + 4 * tid) = sreg;
-      else *reinterpret_cast<uint32_t*>(lsb + 4 * (tid - 128)) = sreg;
+      if (tid < 128) *reinterpret_cast<uint32_t*>(lsa + 4 * tid) = g.s;
+      else *reinterpret_cast<uint32_t*>(lsb + 4 * (tid - 128)) = g.s;
     };
 
     f32x16_t acc[2][2];
@@ -264,13 +271,11 @@ __global__ __launch_bounds__(256, 2) void fp8_gemm_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
 
-    load_step(0);
-    store_step(0);
-    __syncthreads();
-    for (int kb = 0; kb < nk; ++kb) {
-      const int buf = kb & 1;
-      load_step(min(kb + 1, nk - 1));  // unconditional (the last step reloads itself)
-      const uint8_t* la = lds8 + buf * kF8Buf;
+    auto iter = [&](auto P_, int kb) {
+      constexpr int P = decltype(P_)::value;
+      load_step(stg[P], min(kb + 2, nk - 1));  // unconditional (clamped)
+      __builtin_amdgcn_sched_barrier(0);
+      const uint8_t* la = lds8 + P * kF8Buf;
       const uint8_t* lb = la + kF8Tile;
       const uint8_t* lsa = lb + kF8Tile;
       const uint8_t* lsb = lsa + kF8Scl;
@@ -295,8 +300,18 @@ __global__ __launch_bounds__(256, 2) void fp8_gemm_kernel(
 #pragma unroll
           for (int b = 0; b < 2; ++b) acc[a][b] = mfma_scale_32x32x64_fp8(av[a], bv[b], acc[a][b], sa[a], sbv[b]);
       }
-      if (kb + 1 < nk) store_step(buf ^ 1);
+      __builtin_amdgcn_sched_barrier(0);  // the store of step kb + 1 after this step's MFMAs
+      if (kb + 1 < nk) store_step(stg[P ^ 1], P ^ 1);
       __syncthreads();
+    };
+
+    load_step(stg[0], 0);
+    load_step(stg[1], min(1, nk - 1));
+    store_step(stg[0], 0);
+    __syncthreads();
+    for (int kb = 0; kb < nk; kb += 2) {  // nk is even (K is a multiple of 256)
+      iter(std::integral_constant<int, 0>{}, kb);
+      iter(std::integral_constant<int, 1>{}, kb + 1);
     }
 
     // ---- epilogue
