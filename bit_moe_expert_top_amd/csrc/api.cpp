@@ -186,6 +186,8 @@ moe_status ffn_check(const moe_weights* w, const uint16_t* x, int32_t T, int32_t
   if ((int64_t)T * k >= ((int64_t)1 << 31)) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!x || !counts || !offsets || !perm || !y_perm) return MOE_ERR_INVALID_ARG;
+  // the kernels address x (T x H bf16) and one item's rows of h with 32-bit byte offsets
+  if ((int64_t)T * w->H * 2 >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
   const FfnLayout L = ffn_layout(w, T, k);
   if (!ws || ws_bytes < L.fixed) return MOE_ERR_WORKSPACE;
   if (w->n_hot > 0 && ffn_slots(w, L, ws_bytes) < 1) return MOE_ERR_WORKSPACE;

@@ -240,7 +240,10 @@ __device__ __forceinline__ void stream_task(const uint8_t* __restrict__ codes,
   // per-expert buffers (uniform base, byte size) and per-lane byte offsets
   const buf_rsrc rc = make_rsrc(codes + ebase * cbr, (uint32_t)rows_per_expert * cbr);
   const buf_rsrc rs = make_rsrc(scales + ebase * sbr, (uint32_t)rows_per_expert * sbr);
-  const buf_rsrc rb = make_rsrc(bsrc, bsrc_bytes);
+  // FC1 gathers token rows of x (all of x is addressable, < 4 GiB); FC2 reads the item's own h
+  // rows, so its resource is based at row r0 (h may exceed 4 GiB)
+  const buf_rsrc rb = FC == 1 ? make_rsrc(bsrc, bsrc_bytes)
+                              : make_rsrc(bsrc + (size_t)r0 * K, (uint32_t)nrows * (uint32_t)K * 2u);
   uint32_t coff[kRT], soff[kRT];
 #pragma unroll
   for (int t = 0; t < kRT; ++t) {
@@ -261,7 +264,7 @@ __device__ __forceinline__ void stream_task(const uint8_t* __restrict__ codes,
     const int c = pos ^ (n & 7);
     // unconditional (clamped) row lookups, so the eight loads issue together
     const int nn = min(n, nrows - 1);
-    const uint32_t rowb = FC == 1 ? (uint32_t)(perm[r0 + nn] / ktop) : (uint32_t)(r0 + nn);
+    const uint32_t rowb = FC == 1 ? (uint32_t)(perm[r0 + nn] / ktop) : (uint32_t)nn;
     const uint32_t o = (rowb * (uint32_t)K + (uint32_t)(256 * n_it * p) + 64u * G * (uint32_t)(c >> 3)) * 2u +
                        16u * (uint32_t)(c & 7);
     doff[u] = (u < nrounds && n < nrows) ? o : kOffNone;
@@ -427,7 +430,7 @@ hipError_t launch_lowbit_fc2(const LowbitWeights& w, int E, int H, int I, int k,
   (void)E;
   const int ks = k_split_for(T, I);
   const int64_t tasks = (int64_t)max_items * ((H / 64) / (4 / ks));
-  const uint32_t hb = (uint32_t)((size_t)T * k * I * 2);
+  const uint32_t hb = 0;  // unused: FC2 bases its resource at each item's rows
   if (w.fmt == W2Fmt::kId)
     return launch_stream<W2Fmt, 2>(w.w2_codes, w.w2_scales, H, I, H, 1, hbuf, nullptr, plan, hb, ks, tasks, s, y);
   if (w.fmt == W3Fmt::kId)

@@ -133,7 +133,8 @@ moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
  *            the largest that fits in ws_bytes, capped at n_hot, and the hot experts are
  *            converted and computed in batches of that many (at least one slot must fit).
  *   hot_ids  must be distinct expert ids in [0, E) (not checked: device memory).
- * Requirements: H % 256 == 0, I % 256 == 0, H and I <= 16384; fmt W2 or W3.
+ * Requirements: H % 256 == 0, I % 256 == 0, H and I <= 16384; fmt W2 or W3; T * H * 2 < 2^32
+ * (x is addressed with 32-bit byte offsets; larger batches return UNSUPPORTED: split them).
  * Errors: INVALID_ARG, UNSUPPORTED (format/shape not built), WORKSPACE. */
 size_t moe_expert_ffn_ws_bytes(const moe_weights* w, int32_t T, int32_t k, int32_t fp8_slots);
 moe_status moe_expert_ffn(const moe_weights* w, const uint16_t* x, int32_t T, int32_t k,

@@ -83,3 +83,15 @@ def test_ffn_argument_checks(lib):
     hot_missing = L.MoeWeights(8, 256, 512, L.MOE_FMT_W2, p, p, p, p, 2, None, None, None, None, None)
     assert L.lib.moe_expert_ffn(ctypes.byref(hot_missing), p, 16, 2, p, p, p, p, p, 1 << 30, None) == -1
     assert L.lib.moe_debug_dequant(ctypes.byref(w), 8, 1, p, None) == -1  # expert out of range
+
+
+def test_ffn_rejects_batches_beyond_32bit_offsets(lib):
+    import sys
+    sys.path.insert(0, ROOT)
+    from bit_moe_expert_top_amd import _lib as L
+
+    p = 16
+    w = L.MoeWeights(8, 4096, 512, L.MOE_FMT_W2, p, p, p, p, 0, None, None, None, None, None)
+    T = (1 << 32) // (4096 * 2)  # T * H * 2 == 2^32
+    assert L.lib.moe_expert_ffn(ctypes.byref(w), p, T, 1, p, p, p, p, p, 1 << 40, None) == -2
+    assert L.lib.moe_expert_ffn(ctypes.byref(w), p, T - 1, 1, p, p, p, p, p, 10, None) == -3  # ws check next

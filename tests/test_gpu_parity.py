@@ -142,7 +142,7 @@ def test_layer_decode_shape_gemm_path(L, T, sample):
     _check_layer(L, "decode", T, sample)
 
 
-@pytest.mark.parametrize("T,sample", [(8192, [0, 4097, 8191])])
+@pytest.mark.parametrize("T,sample", [(8192, [0, 4097, 8191]), (65536, [0, 32768, 65535])])
 def test_layer_prefill(L, T, sample):
     _check_layer(L, "prefill", T, sample)
 
