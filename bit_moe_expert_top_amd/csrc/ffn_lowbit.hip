@@ -244,6 +244,12 @@ __device__ __forceinline__ void stream_task(const uint8_t* __restrict__ codes,
   // rows, so its resource is based at row r0 (h may exceed 4 GiB)
   const buf_rsrc rb = FC == 1 ? make_rsrc(bsrc, bsrc_bytes)
                               : make_rsrc(bsrc + (size_t)r0 * K, (uint32_t)nrows * (uint32_t)K * 2u);
+  // Source row of each of the item's (<= 32) tokens: lane i looks up token i once (one
+  // branch-free load, issued before the prologue's code loads so the two latencies overlap),
+  // and the B rounds below read it from that lane.
+  uint32_t lane_row = (uint32_t)min(lane & 31, nrows - 1);
+  uint32_t perm_v = 0;
+  if constexpr (FC == 1) perm_v = (uint32_t)perm[r0 + (int)lane_row];
   uint32_t coff[kRT], soff[kRT];
 #pragma unroll
   for (int t = 0; t < kRT; ++t) {
@@ -252,6 +258,16 @@ __device__ __forceinline__ void stream_task(const uint8_t* __restrict__ codes,
     coff[t] = (uint32_t)row * cbr + F::code_bytes((uint32_t)(k0 + 64 * G * q));
     soff[t] = (uint32_t)row * sbr + F::scale_bytes((uint32_t)(k0 + 64 * G * q));
   }
+  Pipe<F, NT, G> P;
+#pragma unroll
+  for (int t = 0; t < kRT; ++t)
+#pragma unroll
+    for (int bt = 0; bt < NT; ++bt) P.acc[t][bt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // prologue: scales and codes of super-step 0 (B of step 0 below, once its rows are known)
+  load_scales<F, NT, G>(P, rs, soff, 0);
+  load_codes<F, NT, G>(P, 0, rc, coff, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (FC == 1) lane_row = perm_v / (uint32_t)ktop;
   // B stage: KS parts x 16*NT tokens x 32 chunks of 16 bytes; chunk c of token n sits at
   // position c ^ (n & 7) of the token's 512 bytes.
   const int per_part = NT * 16 * 32;    // chunks per K part
@@ -262,9 +278,8 @@ __device__ __forceinline__ void stream_task(const uint8_t* __restrict__ codes,
     const int f = 256 * u + 64 * w + lane;
     const int p = f / per_part, rem = f - p * per_part, n = rem >> 5, pos = rem & 31;
     const int c = pos ^ (n & 7);
-    // unconditional (clamped) row lookups, so the eight loads issue together
     const int nn = min(n, nrows - 1);
-    const uint32_t rowb = FC == 1 ? (uint32_t)(perm[r0 + nn] / ktop) : (uint32_t)nn;
+    const uint32_t rowb = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * nn, (int)lane_row);
     const uint32_t o = (rowb * (uint32_t)K + (uint32_t)(256 * n_it * p) + 64u * G * (uint32_t)(c >> 3)) * 2u +
                        16u * (uint32_t)(c & 7);
     doff[u] = (u < nrounds && n < nrows) ? o : kOffNone;
@@ -284,14 +299,6 @@ __device__ __forceinline__ void stream_task(const uint8_t* __restrict__ codes,
     for (int o = 0; o < 8; ++o)
       bread[bt * 8 + o] = (uint32_t)(kpart * per_part * 16 + (16 * bt + i16) * 512 + 16 * ((8 * q + o) ^ (i16 & 7)));
 
-  Pipe<F, NT, G> P;
-#pragma unroll
-  for (int t = 0; t < kRT; ++t)
-#pragma unroll
-    for (int bt = 0; bt < NT; ++bt) P.acc[t][bt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // prologue: scales and codes of super-step 0, B of step 0
-  load_scales<F, NT, G>(P, rs, soff, 0);
-  load_codes<F, NT, G>(P, 0, rc, coff, 0);
   dma_b<G>(rb, bs0, doff, active, wu, 0);
   __builtin_amdgcn_sched_barrier(0);
   const int n_ss = n_it / G;
