@@ -19,8 +19,12 @@ inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 inline moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 // Rows per work item of the streaming kernels: a group of one expert is split into items
-// of at most 32 rows (two 16-token MFMA tiles).
+// of at most 32 rows (two 16-token MFMA tiles); in batches of <= 16 tokens at most 16 rows:
+// there the streaming kernel splits K across its waves and its token stage holds one 16-row
+// tile per K part.  (With distinct experts per token a group never exceeds T rows; repeated
+// ids can make it larger.)
 constexpr int kStreamChunk = 32;
+inline int stream_chunk(int T) { return T <= 16 ? 16 : kStreamChunk; }
 // In batches of at least this many tokens, the groups larger than kStreamChunk rows run on the
 // grouped-GEMM kernels (items of kGemmRows rows); smaller groups always stream.
 constexpr int kGemmMinTokens = 128;
@@ -44,7 +48,8 @@ FfnLayout ffn_layout(const moe_weights* w, int T, int k) {
   const int64_t R = (int64_t)T * k;
   L.gemm = T >= kGemmMinTokens;
   const int64_t per_expert = R < w->E ? R : w->E;  // one partial item per expert at most
-  L.max_items_s = (R + kStreamChunk - 1) / kStreamChunk + per_expert;
+  const int chunk = stream_chunk(T);
+  L.max_items_s = (R + chunk - 1) / chunk + per_expert;
   L.max_items_g = L.gemm ? (R + kGemmRows - 1) / kGemmRows + per_expert : 0;
   size_t off = 0;
   L.plan_s_off = off;
@@ -221,7 +226,7 @@ moe_status ffn_run_stage(const moe_weights* w, const uint16_t* x, int32_t T, int
   hipError_t e = hipSuccess;
   switch (stage) {
     case 0:
-      e = launch_prepare(offsets, w->E, kStreamChunk, kGemmRows, L.gemm, w->hot_ids, w->n_hot, plan_s, plan_g,
+      e = launch_prepare(offsets, w->E, stream_chunk(T), kGemmRows, L.gemm, w->hot_ids, w->n_hot, plan_s, plan_g,
                          x, T, w->H, lw.fmt, xp, s);
       break;
     case 1:

@@ -132,6 +132,30 @@ def test_layer_tiny_k1_and_kE(L):
     _check_layer(L, "tiny", 9, k=8)
 
 
+@pytest.mark.parametrize("T", [1, 2, 10, 40])
+def test_ffn_repeated_expert_ids(L, T):
+    """Ids supplied directly, with experts repeated within a token: a group then holds more
+    than T rows, and the streaming path must still split it into items its token stage holds
+    (at most 8 rows when K is split in 4, 16 when split in 2)."""
+    # decode-sized experts (FC1 K = 4096, FC2 K = 2048) so every K split is taken
+    name, k, ov = "tiny", 8, dict(H=4096, I=2048)
+    sp, dw = device_layer(name, k=k, **ov)
+    lay = oracle_layer(name, k=k, **ov)
+    b = moegen.batch(sp, T)
+    r = np.random.default_rng(1234 + T)
+    ids = np.where(r.uniform(size=(T, k)) < 0.75, 3, r.integers(0, sp["E"], size=(T, k))).astype(np.int32)
+    counts, offsets, perm, inv = OM.permute(ids, sp["E"])
+    assert counts.max() > T  # the case under test
+    c_d, o_d, p_d, i_d = L.moe_permute(to_dev(ids), sp["E"])
+    np.testing.assert_array_equal(host(o_d), offsets)
+    np.testing.assert_array_equal(host(p_d), perm)
+    y = host(L.moe_expert_ffn(dw, to_dev(b["x"]), k, c_d, o_d, p_d))
+    want = OM.expert_ffn(lay, b["x"], k, offsets, perm, experts=sorted(set(ids.reshape(-1).tolist())))
+    err = max_err_over_rms(y, want)
+    print(f"repeated ids T={T}: max|err|/rms = {err:.4g}", flush=True)
+    assert err <= TOL_BF16
+
+
 @pytest.mark.parametrize("T,sample", [(1, None), (8, None), (64, [0, 31, 63])])
 def test_layer_decode(L, T, sample):
     _check_layer(L, "decode", T, sample)
