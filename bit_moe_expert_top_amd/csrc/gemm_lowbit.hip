@@ -5,21 +5,28 @@
 // routed rows of each expert.  [Moet-QA]: 2-bit codes on {-4,-1,1,4}, a bf16 scale per 32
 // along K.  [Strata-R9700] path 6: 3-bit codes on eight levels, an e4m3 scale / 64 per 64.
 //
-// Work item = (row tile of <= 128 grouped rows of one expert, column tile of 256 weight rows).
-// A workgroup of 8 waves (2 x 4) computes the 128 x 256 tile with v_mfma_f32_32x32x16_bf16,
-// each wave 64 x 64 (2 x 2 MFMA tiles).  Per 64-wide K step the workgroup loads the token rows
-// (16 KB, gathered) and the packed codes of its 256 weight rows, decodes the codes to exact
-// bf16 into LDS (the same decode as the streaming kernels, lowbit_fmt.h), and runs 16 MFMAs
-// per wave; LDS is double buffered and the global loads run two steps ahead.  The token rows
-// are the traffic that bounds this kernel (the weights are 2-3 bits), so the tile is wide in
-// N, and the column tiles of one item are given to the workgroups of one XCD (workgroups are
-// dispatched to the 8 XCDs round robin), so its token rows are fetched into that XCD's L2 once.
+// Work item = (row tile of <= 128 grouped rows of one expert, column tile of the weight rows).
+// A workgroup has 8 waves; every wave computes all 128 rows x its own 32*NCT weight columns with
+// v_mfma_f32_32x32x16_bf16 (4 x NCT MFMA tiles).  The weights never pass through LDS: each lane
+// loads and decodes straight into its MFMA B registers the 32-k field it supplies (lane l:
+// weight row l % 32 of a column tile, k-half l / 32 of every 64-k step; for 2-bit codes that is
+// exactly one scale group), with the format's own decode (lowbit_fmt.h).  Only the token rows
+// (the A operand, shared by the 8 waves) are staged in LDS: direct global -> LDS loads into a
+// four-deep ring, 16-byte chunks XOR-swizzled by row / 2 (conflict-free reads of 128-byte rows),
+// one barrier per 64-k step; the packed codes and scales run in a four-slot register ring; both
+// are fetched two steps ahead.  Per MFMA the LDS carries
+// 0.5 KB of A reads (no B writes or reads), so the matrix cores rather than LDS bound the step.
+// Work is handed out in blocks of 4 consecutive items x all column tiles, one block to the
+// workgroups of one XCD at a time (workgroups are dispatched to the 8 XCDs round robin), so
+// the weights of a column tile are shared through that XCD's L2 by the block's items (mostly
+// of one expert: items are consecutive row chunks) and an item's token rows by its tiles.
 // Token operand and decoded weights share the format's k-slot order: x comes permuted from the
 // prepare kernel and FC1 writes h permuted, so A and B always agree.
-//   FC1 column tile n: wave column wn holds gate rows 128n + 32wn + [0,32) and the up rows
-//       I + 128n + 32wn + [0,32) as its two MFMA column tiles, so gate and up of one h column
-//       sit in the same lane and SwiGLU is applied in the epilogue (h stored bf16).
-//   FC2 column tile n: weight rows 256n + [0,256); the epilogue stores y (fp32).
+//   FC1 column tile n (NCT = 2): wave w holds gate rows 256n + 32w + [0,32) and up rows
+//       I + 256n + 32w + [0,32) as its two MFMA column tiles, so gate and up of one h column sit
+//       in the same lane and register and SwiGLU is applied in the epilogue (h stored bf16).
+//   FC2 column tile n: weight rows 256*NCT*n + 32*NCT*w + 32c + [0,32) (NCT = 2 when H is a
+//       multiple of 512, else 1); the epilogue stores y (fp32).
 #include <type_traits>
 
 #include "common.h"
@@ -38,203 +45,308 @@ __device__ __forceinline__ f32x16 mfma_32x32x16_bf16(u32x4 a, u32x4 b, f32x16 c)
                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-constexpr int kBM = 128, kBN = 256, kBK = 64, kThreads = 512;
-constexpr int kLdsRow = kBK + 8;                   // bf16 per LDS row (16 B of padding)
-constexpr int kATile = kBM * kLdsRow;              // A tile (bf16 elements)
-constexpr int kBufElems = (kBM + kBN) * kLdsRow;   // A + B tiles of one buffer
-constexpr int kGemmLds = 2 * kBufElems * 2;        // 2 buffers x bf16 = 110,592 B
-constexpr int kGemmGrid = 256;                     // one workgroup per CU, 32 per XCD
+constexpr int kBM = 128, kBK = 64, kThreads = 512;
+constexpr int kAStage = kBM * kBK * 2;  // one step of token rows (bf16): 16 KB
+constexpr int kAStages = 4;             // a ring as deep as the code ring: stage = step % 4, static
+constexpr int kGemmGrid = 256;          // one workgroup per CU, 32 per XCD
+typedef __attribute__((address_space(3))) void lds_void_t;
 
-template <class F, int FC>
+// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt not waited on)
+template <int N>
+__device__ __forceinline__ void gemm_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | 0xF00 | ((N >> 4) << 14));
+}
+
+// One lane's 32-k field of one weight row for one step: the packed code words and the scale.
+template <class F>
+struct Field {
+  uint32_t c[F::kFieldWords];
+  uint32_t s;
+};
+// vector loads per field (the waits below count them)
+template <class F>
+constexpr int field_loads() { return F::kFieldWords == 3 ? 3 : 2; }
+
+template <class F>
+__device__ __forceinline__ void load_field(Field<F>& g, buf_rsrc rc, buf_rsrc rs, uint32_t co, uint32_t so) {
+  const uint64_t c01 = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rc, (int)co, 0, 0));
+  g.c[0] = (uint32_t)c01;
+  g.c[1] = (uint32_t)(c01 >> 32);
+  if constexpr (F::kFieldWords == 3) g.c[2] = buf_load4(rc, co + 8u);
+  if constexpr (F::kId == W2Fmt::kId)
+    g.s = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, (int)so, 0, 0);
+  else
+    g.s = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, (int)so, 0, 0);
+}
+
+template <class F, int FC, int NCT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int rows_per_expert,
     int K, int width, int ktop, const uint16_t* __restrict__ asrc, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ plan, uint32_t asrc_bytes, void* __restrict__ out) {
-  extern __shared__ __align__(16) uint16_t lds[];
-  const int tid = threadIdx.x, lane = wave_lane(), w = tid / kWave;
-  const int wm = w & 1, wn = w >> 1;
+  static_assert(FC == 2 || NCT == 2, "FC1 pairs a gate and an up column tile per wave");
+  // one __shared__ object per stage: the compiler tracks the direct-to-LDS loads per object, so a
+  // read of one stage waits only for that stage's loads (one array would wait for all of them)
+  __shared__ __align__(16) uint8_t as0[kAStage];
+  __shared__ __align__(16) uint8_t as1[kAStage];
+  __shared__ __align__(16) uint8_t as2[kAStage];
+  __shared__ __align__(16) uint8_t as3[kAStage];
+  auto stage_ptr = [&](auto T_) -> uint8_t* {
+    constexpr int T = decltype(T_)::value;
+    return T == 0 ? as0 : (T == 1 ? as1 : (T == 2 ? as2 : as3));
+  };
+  int lane = wave_lane();
+  asm volatile("" : "+v"(lane));  // lane-derived offsets are recomputed per tile, not held
+  const int w = threadIdx.x / kWave;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int i32 = lane & 31, hk = lane >> 5;
   const int n_items = plan[0];
   const int4* items = reinterpret_cast<const int4*>(plan + 4);
-  const int n_ntiles = FC == 1 ? width / 128 : rows_per_expert / kBN;
+  const int n_ntiles = FC == 1 ? width / 256 : rows_per_expert / (256 * NCT);
   const uint32_t cbr = F::code_bytes((uint32_t)K), sbr = F::scale_bytes((uint32_t)K);
-  const int nk = K / kBK;
-  // XCD-aware order: the workgroups of XCD x (blockIdx % 8, for a grid that is a multiple of 8)
-  // take the items x, x + 8, ..., all column tiles of an item in a row
+  const int nk = K / kBK;  // a multiple of 4 (K is a multiple of 256)
+  constexpr int kLoadsPerStep = NCT * field_loads<F>() + 2;  // code/scale loads + 2 token-row loads
+  // XCD-aware order: item blocks b = x, x + 8, ... go to XCD x (blockIdx % 8, for a grid that
+  // is a multiple of 8); within a block the work runs column tile by column tile, the items of
+  // the block side by side
+  constexpr int kIB = 4;  // items per block
   const int xcd = blockIdx.x & 7, nb_x = gridDim.x >> 3, lb = blockIdx.x >> 3;
-  const int items_x = n_items > xcd ? (n_items - xcd + 7) >> 3 : 0;
-  const int total_x = items_x * n_ntiles;
+  const int n_blocks = (n_items + kIB - 1) / kIB;
+  const int blocks_x = n_blocks > xcd ? (n_blocks - xcd + 7) >> 3 : 0;
+  const int per_block = kIB * n_ntiles;
+  const int total_x = blocks_x * per_block;
 
   for (int p = lb; p < total_x; p += nb_x) {
-    const int item = xcd + 8 * (p / n_ntiles), nt_i = p % n_ntiles;
+    const int bl = p / per_block, rem = p - bl * per_block;
+    const int nt_i = rem / kIB, item = (xcd + 8 * bl) * kIB + (rem - nt_i * kIB);
+    if (item >= n_items) continue;  // the last block may be short (uniform per workgroup)
     const int4 itm = items[item];
     const int e = itm.x, r0 = itm.y, nrows = itm.z;
     const size_t ebase = (size_t)e * rows_per_expert;
 
-    // ---- per-thread load assignments for this tile (uniform buffer bases, per-lane offsets)
-    // A: 128 rows x 8 chunks of 16 B per K step; thread owns rows (tid >> 3) + 64 u (u = 0, 1),
-    //    chunk tid & 7.  FC1 gathers token rows of x (all of x is addressable); FC2 reads h
-    //    rows r0.. of this tile (based at r0: h may reach 2 GiB).
+    // ---- token rows (A): wave w loads rows 16w + 8u + lane/8 (u = 0, 1), 16-byte chunk
+    //      position lane % 8 <- source chunk (lane % 8) ^ ((row / 2) % 8).  FC1 gathers rows of x (all
+    //      of x is addressable); FC2 reads h rows r0.. of this tile (based at r0: h may reach 2 GiB)
     const buf_rsrc ra = FC == 1 ? make_rsrc(asrc, asrc_bytes)
                                 : make_rsrc(asrc + (size_t)r0 * K, (uint32_t)nrows * K * 2u);
-    uint32_t aoff[2];
+    int arow[2];
+    uint32_t tok[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int r = (tid >> 3) + 64 * u;
-      const int rr = min(r, nrows - 1);
-      const uint32_t tok = FC == 1 ? (uint32_t)(perm[r0 + rr] / ktop) : (uint32_t)rr;
-      aoff[u] = r < nrows ? (tok * (uint32_t)K + 8u * (tid & 7)) * 2u : kOffNone;
+      arow[u] = 16 * w + 8 * u + (lane >> 3);
+      const int rr = min(arow[u], nrows - 1);
+      tok[u] = FC == 1 ? (uint32_t)perm[r0 + rr] : (uint32_t)rr;  // branch-free, issued first
     }
-    // B: weight row j = tid >> 1 of the tile, half h = tid & 1 of its 64 codes (32 codes).
-    const int j = tid >> 1, hsel = tid & 1;
-    int wrow;
-    if (FC == 1) {
-      const int jw = j >> 6, jj = j & 63;  // wave column, position in it
-      wrow = (jj < 32 ? 128 * nt_i + 32 * jw + jj : width + 128 * nt_i + 32 * jw + (jj - 32));
-    } else {
-      wrow = kBN * nt_i + j;
-    }
+    // ---- weights (B): column tile c of this lane is weight row wrow[c]; per step the lane
+    //      supplies one 32-k field of it.  2-bit codes come in groups of 4 steps (256 k): the
+    //      lane's k-half hk owns the contiguous k [128 hk, 128 hk + 128) of the group, 32 k per
+    //      step, so its 32 code bytes and 4 scales are fetched once per group (two 16-byte loads
+    //      and one 8-byte load; the two halves of a row ask for 64 contiguous bytes at once,
+    //      rather than 16 bytes of a different line every step).  3-bit codes come per step, the
+    //      half hk owning k [32 hk, 32 hk + 32) of the step.  The token rows follow the same map.
+    constexpr bool kGroup = F::kId == W2Fmt::kId;
     const buf_rsrc rc = make_rsrc(codes + ebase * cbr, (uint32_t)rows_per_expert * cbr);
     const buf_rsrc rs = make_rsrc(scales + ebase * sbr, (uint32_t)rows_per_expert * sbr);
-    const uint32_t coff = (uint32_t)wrow * cbr + F::code_bytes(32u * hsel);
-    // 2-bit: the half's own bf16 scale; 3-bit: the step's one scale byte (shared by both halves)
-    const uint32_t soff = (uint32_t)wrow * sbr + (F::kId == W2Fmt::kId ? 2u * hsel : 0u);
+    uint32_t coff[NCT], soff[NCT];
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+      const int wrow = FC == 1 ? (c == 0 ? 256 * nt_i + 32 * w + i32 : width + 256 * nt_i + 32 * w + i32)
+                               : 256 * NCT * nt_i + 32 * NCT * w + 32 * c + i32;
+      if constexpr (kGroup) {
+        coff[c] = (uint32_t)wrow * cbr + F::code_bytes(128u * hk);
+        soff[c] = (uint32_t)wrow * sbr + F::scale_bytes(128u * hk);
+      } else {
+        coff[c] = (uint32_t)wrow * cbr + F::code_bytes(32u * hk);
+        soff[c] = (uint32_t)wrow * sbr;  // one scale byte per step, shared by both halves
+      }
+    }
     const uint32_t cstep = F::code_bytes(kBK), sstep = F::scale_bytes(kBK);
-
-    // register staging of K steps, two deep: the loads of step kb + 2 are issued while step kb
-    // is computed from LDS and step kb + 1 waits in registers to be stored
-    struct Staged {
-      u32x4 a[2];
-      uint32_t c[F::kFieldWords];
-      uint32_t s;
+    // 2-bit: one lane's group (32 code bytes, 4 bf16 scales), in a two-slot ring (group g in
+    // slot g % 2); 3-bit: one lane's field per step, in a four-slot ring (step kb in slot kb % 4)
+    struct Group {
+      uint32_t c[8];
+      uint32_t s[2];
     };
-    Staged stg[2];
-    auto load_step = [&](Staged& g, int kb) {
+    Group gr[kGroup ? 2 : 1][NCT];
+    Field<F> fr[kGroup ? 1 : 4][NCT];
+    auto load_group = [&](Group* gp, int g) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) g.a[u] = buf_load16(ra, aoff[u] + (uint32_t)kb * kBK * 2u);
-      const uint32_t co = coff + (uint32_t)kb * cstep, so = soff + (uint32_t)kb * sstep;
-      const uint64_t c01 = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rc, (int)co, 0, 0));
-      g.c[0] = (uint32_t)c01;
-      g.c[1] = (uint32_t)(c01 >> 32);
-      if constexpr (F::kFieldWords == 3) g.c[2] = buf_load4(rc, co + 8u);
-      if constexpr (F::kId == W2Fmt::kId)
-        g.s = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, (int)so, 0, 0);
-      else
-        g.s = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, (int)so, 0, 0);
-    };
-    auto store_a = [&](const Staged& g, int buf) {
-      uint16_t* la = lds + buf * kBufElems;
+      for (int c = 0; c < NCT; ++c) {
+        const uint32_t co = coff[c] + (uint32_t)g * (4u * cstep), so = soff[c] + (uint32_t)g * (4u * sstep);
+        const u32x4 lo = buf_load16(rc, co), hi = buf_load16(rc, co + 16u);
+        const uint64_t sc = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rs, (int)so, 0, 0));
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int r = (tid >> 3) + 64 * u;
-        *reinterpret_cast<u32x4*>(la + r * kLdsRow + 8 * (tid & 7)) = g.a[u];
-      }
-    };
-    // operand op (0..3) of the thread's 32 codes -> its 8 slots of the B tile
-    auto store_b = [&](const Staged& g, const typename F::Tab& tab, int buf, int op) {
-      uint16_t* dst = lds + buf * kBufElems + kATile + j * kLdsRow + 32 * hsel;
-      *reinterpret_cast<u32x4*>(dst + 8 * op) = F::decode32(g.c, tab, op);
-    };
-    auto store_step = [&](const Staged& g, int buf) {
-      store_a(g, buf);
-      const typename F::Tab tab = F::table32(g.s);
-#pragma unroll
-      for (int op = 0; op < 4; ++op) store_b(g, tab, buf, op);
-    };
-
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
-
-    // one K step from LDS buffer P; staging slot P is refilled with step kb + 2, and step kb + 1
-    // (slot P^1) is stored into the other LDS buffer in quarters between this step's MFMA
-    // groups, so the decode's VALU work overlaps the matrix cores.  The operands of sub-step
-    // kk + 1 are read from LDS before the MFMAs of kk.  Loads are unconditional (clamped).
-    auto iter = [&](auto P_, int kb) {
-      constexpr int P = decltype(P_)::value;
-      load_step(stg[P], min(kb + 2, nk - 1));
-      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this step's LDS reads
-      const uint16_t* la = lds + P * kBufElems;
-      const uint16_t* lbm = la + kATile;
-      const bool more = kb + 1 < nk;
-      u32x4 av[2][2], bv[2][2];
-      auto read_ops = [&](int kk, u32x4* a_, u32x4* b_) {
-        const int kof = 16 * kk + 8 * (lane >> 5);
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          a_[t] = *reinterpret_cast<const u32x4*>(la + (64 * wm + 32 * t + (lane & 31)) * kLdsRow + kof);
-          b_[t] = *reinterpret_cast<const u32x4*>(lbm + (64 * wn + 32 * t + (lane & 31)) * kLdsRow + kof);
+        for (int i = 0; i < 4; ++i) {
+          gp[c].c[i] = lo[i];
+          gp[c].c[4 + i] = hi[i];
         }
-      };
-      read_ops(0, av[0], bv[0]);
-      typename F::Tab tab{};
-      if (more) {
-        store_a(stg[P ^ 1], P ^ 1);
-        tab = F::table32(stg[P ^ 1].s);
+        gp[c].s[0] = (uint32_t)sc;
+        gp[c].s[1] = (uint32_t)(sc >> 32);
       }
+    };
+    auto load_codes = [&](Field<F>* f, int kb) {
 #pragma unroll
-      for (int kk = 0; kk < kBK / 16; ++kk) {
-        if (kk + 1 < kBK / 16) read_ops(kk + 1, av[(kk + 1) & 1], bv[(kk + 1) & 1]);
+      for (int c = 0; c < NCT; ++c)
+        load_field<F>(f[c], rc, rs, coff[c] + (uint32_t)kb * cstep, soff[c] + (uint32_t)kb * sstep);
+    };
+    constexpr int kGroupLoads = 3 * NCT;  // vector loads per group (2-bit)
+    // first k of the token chunk a lane loads, per step: 2-bit  256 (kb / 4) + 32 (kb % 4),
+    // 3-bit 64 kb; plus, per lane, (128 or 32) * half + 8 * (chunk % 4)
+    auto kstep = [&](int kb) -> uint32_t {
+      return kGroup ? 256u * (uint32_t)(kb >> 2) + 32u * (uint32_t)(kb & 3) : 64u * (uint32_t)kb;
+    };
+    uint32_t aoff[2];
+    // token rows of step kb into stage T
+    auto dma_a = [&](auto T_, int kb) {
+      uint8_t* st = stage_ptr(T_);
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-          for (int b = 0; b < 2; ++b) acc[a][b] = mfma_32x32x16_bf16(av[kk & 1][a], bv[kk & 1][b], acc[a][b]);
-        if (more) store_b(stg[P ^ 1], tab, P ^ 1, kk);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      __syncthreads();
+      for (int u = 0; u < 2; ++u)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(st + 1024 * (2 * wu + u)), 16,
+                                                 (int)(aoff[u] + 2u * kstep(kb)), 0, 0, 0);
     };
 
-    load_step(stg[0], 0);
-    load_step(stg[1], min(1, nk - 1));
-    store_step(stg[0], 0);
-    __syncthreads();
-    for (int kb = 0; kb < nk; kb += 2) {  // nk is even (K is a multiple of 256)
-      iter(std::integral_constant<int, 0>{}, kb);
-      iter(std::integral_constant<int, 1>{}, kb + 1);
+    f32x16 acc[4][NCT];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[m][c][i] = 0.f;
+
+    // prologue: the first codes (they overlap the row lookups), then the token rows
+    constexpr int kPrologueCodeLoads = kGroup ? kGroupLoads : 2 * NCT * field_loads<F>();
+    if constexpr (kGroup) {
+      load_group(gr[0], 0);
+    } else {
+      load_codes(fr[0], 0);
+      load_codes(fr[1], min(1, nk - 1));
+    }
+    if constexpr (FC == 1) gemm_wait_vmcnt<kPrologueCodeLoads>();  // the row lookups
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t rowx = FC == 1 ? tok[u] / (uint32_t)ktop : tok[u];
+      const int pos = lane & 7, src = pos ^ ((arow[u] >> 1) & 7);
+      const uint32_t ka = (kGroup ? 128u : 32u) * (uint32_t)(src >> 2) + 8u * (uint32_t)(src & 3);
+      aoff[u] = arow[u] < nrows ? (rowx * (uint32_t)K + ka) * 2u : kOffNone;
+    }
+    dma_a(std::integral_constant<int, 0>{}, 0);
+    dma_a(std::integral_constant<int, 1>{}, min(1, nk - 1));
+    gemm_wait_vmcnt<2>();  // the first codes and the token rows of step 0 (step 1's may fly)
+
+    // A operand of MFMA tile m at k sub-step kk: row 32m + i32, 16-byte chunk 4hk + kk of the
+    // step (the lane's k-half), stored at chunk position (4hk + kk) ^ ((row / 2) % 8)
+    uint32_t apos[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) apos[kk] = (uint32_t)(i32 * 128 + 16 * ((4 * hk + kk) ^ ((i32 >> 1) & 7)));
+
+    // Step kb (S8 = kb % 8; token stage S = kb % 4; 2-bit group slot P = S8 / 4):
+    //   1. wait for this lane's codes and token rows of step kb (vector loads complete in issue
+    //      order: those issued in step kb - 1 may stay in flight), then a barrier: every wave's
+    //      rows of step kb are in LDS and every wave is done with step kb - 1.  The barrier is a
+    //      bare s_barrier (with a compiler memory clobber): a __syncthreads fence would also
+    //      drain the loads of the next steps still in flight, which nothing reads before their
+    //      own step's wait and barrier;
+    //   2. issue the next codes (2-bit: at a group's first step the next group, into the other
+    //      slot; 3-bit: step kb + 2 into slot (S + 2) % 4) and the token rows of step kb + 2 into
+    //      stage (S + 2) % 4, which held step kb - 2; past the end the last group / step is
+    //      fetched again into those free places, so the load counts never change;
+    //   3. per 16-k sub-step: A from LDS (read one sub-step ahead), B decoded from the field,
+    //      4 x NCT MFMAs.
+    auto step = [&](auto S8_, int kb) {
+      constexpr int S8 = decltype(S8_)::value, S = S8 & 3, P = S8 >> 2;
+      constexpr int kWait = kGroup ? 2 + (S == 1 ? kGroupLoads : 0) : kLoadsPerStep;
+      gemm_wait_vmcnt<kWait>();
+      asm volatile("s_barrier" ::: "memory");
+      const int kn = min(kb + 2, nk - 1);
+      if constexpr (kGroup) {
+        if constexpr (S == 0) load_group(gr[P ^ 1], min((kb >> 2) + 1, (nk >> 2) - 1));
+      } else {
+        load_codes(fr[(S + 2) & 3], kn);
+      }
+      dma_a(std::integral_constant<int, (S + 2) & 3>{}, kn);
+      __builtin_amdgcn_sched_barrier(0);
+      const uint8_t* st = stage_ptr(std::integral_constant<int, S>{});
+      const uint32_t* fw[NCT];
+      typename F::Tab tab[NCT];
+#pragma unroll
+      for (int c = 0; c < NCT; ++c) {
+        if constexpr (kGroup) {
+          fw[c] = &gr[P][c].c[2 * S];
+          tab[c] = F::table32((gr[P][c].s[S >> 1] >> (16 * (S & 1))) & 0xFFFFu);
+        } else {
+          fw[c] = fr[S][c].c;
+          tab[c] = F::table32(fr[S][c].s);
+        }
+      }
+      u32x4 av[2][4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) av[0][m] = *reinterpret_cast<const u32x4*>(st + apos[0] + 4096 * m);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        if (kk + 1 < 4) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            av[(kk + 1) & 1][m] = *reinterpret_cast<const u32x4*>(st + apos[kk + 1] + 4096 * m);
+        }
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) {
+          const u32x4 bv = F::decode32(fw[c], tab[c], kk);
+#pragma unroll
+          for (int m = 0; m < 4; ++m) acc[m][c] = mfma_32x32x16_bf16(av[kk & 1][m], bv, acc[m][c]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // nk is a multiple of 4 (K of 256); two 2-bit groups per pass keep every slot index static
+    int kb = 0;
+    for (; kb + 8 <= nk; kb += 8) {
+      step(std::integral_constant<int, 0>{}, kb);
+      step(std::integral_constant<int, 1>{}, kb + 1);
+      step(std::integral_constant<int, 2>{}, kb + 2);
+      step(std::integral_constant<int, 3>{}, kb + 3);
+      step(std::integral_constant<int, 4>{}, kb + 4);
+      step(std::integral_constant<int, 5>{}, kb + 5);
+      step(std::integral_constant<int, 6>{}, kb + 6);
+      step(std::integral_constant<int, 7>{}, kb + 7);
+    }
+    if (kb < nk) {
+      step(std::integral_constant<int, 0>{}, kb);
+      step(std::integral_constant<int, 1>{}, kb + 1);
+      step(std::integral_constant<int, 2>{}, kb + 2);
+      step(std::integral_constant<int, 3>{}, kb + 3);
     }
 
-    // ---- epilogue
+    // ---- epilogue: lane holds column i32 of each tile, rows 32m + 8(j/4) + 4hk + j%4
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
+    for (int m = 0; m < 4; ++m) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 64 * wm + 32 * a + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      for (int j = 0; j < 16; ++j) {
+        const int row = 32 * m + 8 * (j >> 2) + 4 * hk + (j & 3);
         if (row >= nrows) continue;
         const size_t r = (size_t)(r0 + row);
-        if (FC == 1) {
-          const float gt = acc[a][0][i], up = acc[a][1][i];
+        if constexpr (FC == 1) {
+          const float gt = acc[m][0][j], up = acc[m][1][j];
           const float hv = __fdividef(gt, 1.0f + __expf(-gt)) * up;
-          const int col = 128 * nt_i + 32 * wn + (lane & 31);
-          reinterpret_cast<uint16_t*>(out)[r * width + 32 * (col >> 5) + F::pos32(col & 31)] =
+          reinterpret_cast<uint16_t*>(out)[r * width + 32 * (8 * nt_i + w) + F::pos32(i32)] =
               (uint16_t)f32_to_bf16_rne(hv);
         } else {
 #pragma unroll
-          for (int b = 0; b < 2; ++b)
-            reinterpret_cast<float*>(out)[r * width + kBN * nt_i + 64 * wn + 32 * b + (lane & 31)] =
-                acc[a][b][i];
+          for (int c = 0; c < NCT; ++c)
+            reinterpret_cast<float*>(out)[r * width + 256 * NCT * nt_i + 32 * NCT * w + 32 * c + i32] =
+                acc[m][c][j];
         }
       }
     }
+    __syncthreads();  // every wave is done with the token stages before the next tile fills them
   }
 }
 
-template <class F, int FC>
+template <class F, int FC, int NCT>
 static hipError_t launch_gemm(const void* codes, const void* scales, int rows, int K, int width,
                               int ktop, const uint16_t* asrc, const int32_t* perm,
                               const int32_t* plan, uint32_t asrc_bytes, void* out, hipStream_t s) {
-  // dynamic LDS above 64 KB must be allowed once per kernel instance
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_kernel<F, FC>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  gemm_kernel<F, FC><<<kGemmGrid, kThreads, kGemmLds, s>>>((const uint8_t*)codes, (const uint8_t*)scales, rows,
+  gemm_kernel<F, FC, NCT><<<kGemmGrid, kThreads, 0, s>>>((const uint8_t*)codes, (const uint8_t*)scales, rows,
                                                          K, width, ktop, asrc, perm, plan, asrc_bytes, out);
   return hipGetLastError();
 }
@@ -245,9 +357,9 @@ hipError_t launch_lowbit_gemm_fc1(const LowbitWeights& w, int H, int I, int k, c
   (void)max_items;
   const uint32_t xb = (uint32_t)((size_t)T * H * 2);
   if (w.fmt == W2Fmt::kId)
-    return launch_gemm<W2Fmt, 1>(w.w1_codes, w.w1_scales, 2 * I, H, I, k, xp, perm, plan, xb, hbuf, s);
+    return launch_gemm<W2Fmt, 1, 2>(w.w1_codes, w.w1_scales, 2 * I, H, I, k, xp, perm, plan, xb, hbuf, s);
   if (w.fmt == W3Fmt::kId)
-    return launch_gemm<W3Fmt, 1>(w.w1_codes, w.w1_scales, 2 * I, H, I, k, xp, perm, plan, xb, hbuf, s);
+    return launch_gemm<W3Fmt, 1, 2>(w.w1_codes, w.w1_scales, 2 * I, H, I, k, xp, perm, plan, xb, hbuf, s);
   return hipErrorInvalidValue;
 }
 
@@ -256,10 +368,14 @@ hipError_t launch_lowbit_gemm_fc2(const LowbitWeights& w, int H, int I, int k,
                                   float* y, hipStream_t s) {
   (void)max_items;
   const uint32_t hb = (uint32_t)((size_t)T * k * I * 2);
+  // 512 weight rows per column tile when H allows, else 256 (H is a multiple of 256)
+  const bool wide = H % 512 == 0;
   if (w.fmt == W2Fmt::kId)
-    return launch_gemm<W2Fmt, 2>(w.w2_codes, w.w2_scales, H, I, H, 1, hbuf, nullptr, plan, hb, y, s);
+    return wide ? launch_gemm<W2Fmt, 2, 2>(w.w2_codes, w.w2_scales, H, I, H, 1, hbuf, nullptr, plan, hb, y, s)
+                : launch_gemm<W2Fmt, 2, 1>(w.w2_codes, w.w2_scales, H, I, H, 1, hbuf, nullptr, plan, hb, y, s);
   if (w.fmt == W3Fmt::kId)
-    return launch_gemm<W3Fmt, 2>(w.w2_codes, w.w2_scales, H, I, H, 1, hbuf, nullptr, plan, hb, y, s);
+    return wide ? launch_gemm<W3Fmt, 2, 2>(w.w2_codes, w.w2_scales, H, I, H, 1, hbuf, nullptr, plan, hb, y, s)
+                : launch_gemm<W3Fmt, 2, 1>(w.w2_codes, w.w2_scales, H, I, H, 1, hbuf, nullptr, plan, hb, y, s);
   return hipErrorInvalidValue;
 }
 

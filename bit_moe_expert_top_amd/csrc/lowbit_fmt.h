@@ -54,7 +54,9 @@ __device__ __forceinline__ ScaleBytes<NB> load_scale_bytes(buf_rsrc r, uint32_t 
 // 2 added to the exponent: every weight of a group has the scale's low byte, and a byte table
 // of the four high bytes {-4s, -s, s, 4s} is looked up with one v_perm_b32 per four codes
 // (masking a word shifted by 2u with 0x03030303 leaves codes u, 4+u, 8+u, 12+u one per byte:
-// a selector).  Two more v_perm_b32 interleave the low byte: ~1.2 VALU operations per weight.
+// a selector).  Two more v_perm_b32 interleave the low byte, taken straight from the scale
+// word: ~1.2 VALU operations per weight.  The table itself is one v_perm_b32 (byte broadcast
+// of the high byte and of its sign-flipped copy) and one add per group.
 // Slot order: within every 16 k, slots hold k = 0,4,8,12, 1,5,9,13, 2,6,10,14, 3,7,11,15.
 // =====================================================================================
 struct W2Fmt {
@@ -65,41 +67,47 @@ struct W2Fmt {
   __host__ __device__ static constexpr uint32_t scale_bytes(uint32_t k) { return k / 16; }
 
   struct Codes { u32x4 w; };
-  struct Tab { uint32_t lut[2], lb[2]; };
+  // lut[g]: the four high bytes of group g; sw: the scale word (bf16 of group g in half g)
+  struct Tab { uint32_t lut[2], sw; };
 
   __device__ static __forceinline__ Codes load_codes(buf_rsrc r, uint32_t off) { return {buf_load16(r, off)}; }
 
-  __device__ static __forceinline__ void table1(uint32_t s16, uint32_t& lut, uint32_t& lb) {
-    const uint32_t hb = (s16 >> 8) & 0xFFu;
-    lut = ((hb * 0x01010101u) ^ 0x00008080u) + 0x01000001u;
-    lb = s16 & 0xFFu;
+  // high bytes {-4s, -s, s, 4s} of group g: bytes (hb^0x80)+1, hb^0x80, hb, hb+1 (the sign
+  // flip, the exponent +2 in the high byte); x = sw with both sign bits flipped
+  template <int g>
+  __device__ static __forceinline__ uint32_t lut_of(uint32_t x, uint32_t sw) {
+    return byte_perm(x, sw, g == 0 ? 0x01010505u : 0x03030707u) + 0x01000001u;
   }
   // the step's scale word: bf16 of k [0,32) in the low half, of k [32,64) in the high half
   __device__ static __forceinline__ Tab table(uint32_t sw) {
     Tab t;
-    table1(sw & 0xFFFFu, t.lut[0], t.lb[0]);
-    table1(sw >> 16, t.lut[1], t.lb[1]);
+    const uint32_t x = sw ^ 0x80008000u;
+    t.lut[0] = lut_of<0>(x, sw);
+    t.lut[1] = lut_of<1>(x, sw);
+    t.sw = sw;
     return t;
   }
   template <int NB>
   __device__ static __forceinline__ uint32_t step_scale(const ScaleBytes<NB>& s, int step) { return s.v[step]; }
 
-  // half 0 covers u = 0, 1 and half 1 u = 2, 3; per u: dwords (code u, 4+u), (8+u, 12+u)
-  __device__ static __forceinline__ u32x4 decode_word(uint32_t w, int half, uint32_t lut, uint32_t lb) {
+  // half 0 covers u = 0, 1 and half 1 u = 2, 3; per u: dwords (code u, 4+u), (8+u, 12+u);
+  // the low byte of group g is byte 2g of the scale word sw
+  template <int g>
+  __device__ static __forceinline__ u32x4 decode_word(uint32_t w, int half, uint32_t lut, uint32_t sw) {
     u32x4 r;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int sh = 2 * (2 * half + u);
       const uint32_t hb = byte_perm(0u, lut, (w >> sh) & 0x03030303u);
-      r[2 * u] = byte_perm(lb, hb, 0x01040004u);
-      r[2 * u + 1] = byte_perm(lb, hb, 0x03040204u);
+      r[2 * u] = byte_perm(sw, hb, g == 0 ? 0x01040004u : 0x01060006u);
+      r[2 * u + 1] = byte_perm(sw, hb, g == 0 ? 0x03040204u : 0x03060206u);
     }
     return r;
   }
   // operand o (0..7) of a step: word o/2, half o%2 (o is a constant after unrolling)
   __device__ static __forceinline__ u32x4 decode(const Codes& c, const Tab& t, int o) {
-    const int wd = o >> 1, g = wd >> 1;
-    return decode_word(c.w[wd], o & 1, t.lut[g], t.lb[g]);
+    const int wd = o >> 1;
+    return wd < 2 ? decode_word<0>(c.w[wd], o & 1, t.lut[0], t.sw) : decode_word<1>(c.w[wd], o & 1, t.lut[1], t.sw);
   }
   // slot of k = c (0..31) in its 32-k block, and the k held by slot s
   __host__ __device__ static constexpr int pos32(int c) {
@@ -113,13 +121,13 @@ struct W2Fmt {
   static constexpr int kFieldWords = 2;
   __device__ static __forceinline__ Tab table32(uint32_t s16) {
     Tab t;
-    table1(s16, t.lut[0], t.lb[0]);
+    t.lut[0] = lut_of<0>(s16 ^ 0x8000u, s16);
     t.lut[1] = t.lut[0];
-    t.lb[1] = t.lb[0];
+    t.sw = s16;
     return t;
   }
   __device__ static __forceinline__ u32x4 decode32(const uint32_t* w, const Tab& t, int op) {
-    return decode_word(w[op >> 1], op & 1, t.lut[0], t.lb[0]);
+    return decode_word<0>(w[op >> 1], op & 1, t.lut[0], t.sw);
   }
 };
 

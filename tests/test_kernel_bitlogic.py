@@ -27,20 +27,21 @@ def v_perm_b32(s0: int, s1: int, sel: int) -> int:
     return out
 
 
-# --- 2-bit: the per-group byte table and the decode of one word (ffn_lowbit.hip) ---
-def w2_table(s16):
-    hb = (s16 >> 8) & 0xFF
-    lut = (((hb * 0x01010101) ^ 0x00008080) + 0x01000001) & 0xFFFFFFFF
-    return lut, s16 & 0xFF
+# --- 2-bit: the per-group byte tables and the decode of one word (lowbit_fmt.h) ---
+def w2_table(sw):
+    """Scale word sw (bf16 of group 0 low, group 1 high) -> the two groups' high-byte tables."""
+    x = sw ^ 0x80008000
+    return [(v_perm_b32(x, sw, sel) + 0x01000001) & 0xFFFFFFFF for sel in (0x01010505, 0x03030707)]
 
 
-def w2_decode_word(w, lut, lb):
-    """Eight dwords (two MFMA operands) from one word: for s = 0..3 the high bytes of codes
-    s, 4+s, 8+s, 12+s, then two interleaves with the scale's low byte."""
+def w2_decode_word(w, lut, sw, g):
+    """Eight dwords (two MFMA operands) from one word of group g: for s = 0..3 the high bytes
+    of codes s, 4+s, 8+s, 12+s, then two interleaves with the group's low byte (byte 2g of sw)."""
+    sel = (0x01040004, 0x03040204) if g == 0 else (0x01060006, 0x03060206)
     out = []
     for s in range(4):
         hb = v_perm_b32(0, lut, (w >> (2 * s)) & 0x03030303)
-        out += [v_perm_b32(lb, hb, 0x01040004), v_perm_b32(lb, hb, 0x03040204)]
+        out += [v_perm_b32(sw, hb, sel[0]), v_perm_b32(sw, hb, sel[1])]
     return out  # dword 2s: (codes s, 4+s); dword 2s+1: (codes 8+s, 12+s)
 
 
@@ -48,8 +49,9 @@ def emulate_w2_row(codes_row, scales_row):
     K = len(codes_row) * 16
     out = np.empty(K, dtype=np.uint16)
     for wc, w in enumerate(codes_row.tolist()):
-        lut, lb = w2_table(int(scales_row[wc // 2]))
-        d = w2_decode_word(w, lut, lb)
+        st, g = wc // 4, (wc // 2) % 2  # 64-k step of the word, scale group within the step
+        sw = int(scales_row[2 * st]) | (int(scales_row[2 * st + 1]) << 16)
+        d = w2_decode_word(w, w2_table(sw)[g], sw, g)
         for s in range(4):
             out[16 * wc + s], out[16 * wc + 4 + s] = d[2 * s] & 0xFFFF, d[2 * s] >> 16
             out[16 * wc + 8 + s], out[16 * wc + 12 + s] = d[2 * s + 1] & 0xFFFF, d[2 * s + 1] >> 16
@@ -66,11 +68,17 @@ def test_w2_decode_trick_matches_oracle():
 
 
 def test_w2_decode_trick_golden_words_and_scale_signs():
-    for s16 in (0x3F80, 0xBF80, 0x3BC8, 0xBC78, 0x0080, 0x7E00):
-        for w in (0x00000000, 0x55555555, 0xAAAAAAAA, 0xFFFFFFFF, 0xE4E4E4E4, 0x1B1B1B1B, 0x9C3A71E5):
-            codes = np.array([w, w], np.uint32)
-            got = emulate_w2_row(codes, np.array([s16], np.uint16))
-            want = OF.dequant_w2(codes[None, :], np.array([[s16]], np.uint16))[0]
+    # one 64-k step: words 0, 1 in scale group 0, words 2, 3 in group 1 (its own scale)
+    scales = (0x3F80, 0xBF80, 0x3BC8, 0xBC78, 0x0080, 0x7E00)
+    words = (0x00000000, 0x55555555, 0xAAAAAAAA, 0xFFFFFFFF, 0xE4E4E4E4, 0x1B1B1B1B, 0x9C3A71E5)
+    for i, s16 in enumerate(scales):
+        s16b = scales[(i + 1) % len(scales)]
+        for j, w in enumerate(words):
+            w2 = words[(j + 3) % len(words)]
+            codes = np.array([w, w, w2, w], np.uint32)
+            sc = np.array([s16, s16b], np.uint16)
+            got = emulate_w2_row(codes, sc)
+            want = OF.dequant_w2(codes[None, :], sc[None, :])[0]
             np.testing.assert_array_equal(got, want)
 
 
