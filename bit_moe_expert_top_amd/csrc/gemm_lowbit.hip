@@ -13,8 +13,8 @@
 // exactly one scale group), with the format's own decode (lowbit_fmt.h).  Only the token rows
 // (the A operand, shared by the 8 waves) are staged in LDS: direct global -> LDS loads into a
 // four-deep ring, 16-byte chunks XOR-swizzled by row / 2 (conflict-free reads of 128-byte rows),
-// one barrier per 64-k step; the packed codes and scales run in a four-slot register ring; both
-// are fetched two steps ahead.  Per MFMA the LDS carries
+// one barrier per 64-k step; the packed codes and scales run in a four-slot register ring; codes
+// are fetched two steps ahead, token rows three.  Per MFMA the LDS carries
 // 0.5 KB of A reads (no B writes or reads), so the matrix cores rather than LDS bound the step.
 // Work is handed out in blocks of 4 consecutive items x all column tiles, one block to the
 // workgroups of one XCD at a time (workgroups are dispatched to the 8 XCDs round robin), so
@@ -47,7 +47,7 @@ __device__ __forceinline__ f32x16 mfma_32x32x16_bf16(u32x4 a, u32x4 b, f32x16 c)
 
 constexpr int kBM = 128, kBK = 64, kThreads = 512;
 constexpr int kAStage = kBM * kBK * 2;  // one step of token rows (bf16): 16 KB
-constexpr int kAStages = 4;             // a ring as deep as the code ring: stage = step % 4, static
+// token rows run in a ring of 4 stages (as0..as3): stage = step % 4, a static index
 constexpr int kGemmGrid = 256;          // one workgroup per CU, 32 per XCD
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -106,7 +106,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
   const int n_ntiles = FC == 1 ? width / 256 : rows_per_expert / (256 * NCT);
   const uint32_t cbr = F::code_bytes((uint32_t)K), sbr = F::scale_bytes((uint32_t)K);
   const int nk = K / kBK;  // a multiple of 4 (K is a multiple of 256)
-  constexpr int kLoadsPerStep = NCT * field_loads<F>() + 2;  // code/scale loads + 2 token-row loads
   // XCD-aware order: item blocks b = x, x + 8, ... go to XCD x (blockIdx % 8, for a grid that
   // is a multiple of 8); within a block the work runs column tile by column tile, the items of
   // the block side by side
@@ -232,41 +231,41 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     }
     dma_a(std::integral_constant<int, 0>{}, 0);
     dma_a(std::integral_constant<int, 1>{}, min(1, nk - 1));
-    gemm_wait_vmcnt<2>();  // the first codes and the token rows of step 0 (step 1's may fly)
+    dma_a(std::integral_constant<int, 2>{}, min(2, nk - 1));
+    gemm_wait_vmcnt<4>();  // the first codes and the token rows of step 0 (steps 1, 2 may fly)
+    asm volatile("s_barrier" ::: "memory");
 
     // A operand of MFMA tile m at k sub-step kk: row 32m + i32, 16-byte chunk 4hk + kk of the
     // step (the lane's k-half), stored at chunk position (4hk + kk) ^ ((row / 2) % 8)
     uint32_t apos[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) apos[kk] = (uint32_t)(i32 * 128 + 16 * ((4 * hk + kk) ^ ((i32 >> 1) & 7)));
+    // A operands of two sub-steps (read one sub-step ahead; sub-step 0 of a step is read during
+    // the last sub-step of the step before)
+    u32x4 av[2][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) av[0][m] = *reinterpret_cast<const u32x4*>(as0 + apos[0] + 4096 * m);
 
-    // Step kb (S8 = kb % 8; token stage S = kb % 4; 2-bit group slot P = S8 / 4):
-    //   1. wait for this lane's codes and token rows of step kb (vector loads complete in issue
-    //      order: those issued in step kb - 1 may stay in flight), then a barrier: every wave's
-    //      rows of step kb are in LDS and every wave is done with step kb - 1.  The barrier is a
-    //      bare s_barrier (with a compiler memory clobber): a __syncthreads fence would also
-    //      drain the loads of the next steps still in flight, which nothing reads before their
-    //      own step's wait and barrier;
+    // Step kb (S8 = kb % 8; token stage S = kb % 4; 2-bit group slot P = S8 / 4), four 16-k
+    // sub-steps, each: A from LDS (read one sub-step ahead), B decoded from the field, 4 x NCT
+    // MFMAs.  Before the last sub-step's MFMAs the step hands over to the next one:
+    //   1. wait for this lane's token rows of step kb + 1 and, before a group's first step, its
+    //      codes (vector loads complete in issue order: those issued in step kb may stay in
+    //      flight), then a barrier: every wave's rows of step kb + 1 are in LDS and every wave is
+    //      done with step kb - 1 (it is past sub-step 2 of step kb).  The barrier is a bare
+    //      s_barrier (with a compiler memory clobber): a __syncthreads fence would also drain the
+    //      loads of the next steps still in flight, which nothing reads before their own wait;
     //   2. issue the next codes (2-bit: at a group's first step the next group, into the other
-    //      slot; 3-bit: step kb + 2 into slot (S + 2) % 4) and the token rows of step kb + 2 into
-    //      stage (S + 2) % 4, which held step kb - 2; past the end the last group / step is
-    //      fetched again into those free places, so the load counts never change;
-    //   3. per 16-k sub-step: A from LDS (read one sub-step ahead), B decoded from the field,
-    //      4 x NCT MFMAs.
+    //      slot; 3-bit: step kb + 2 into slot (S + 2) % 4) and the token rows of step kb + 3
+    //      into stage (S + 3) % 4, which held step kb - 1; past the end the last group / step
+    //      is fetched again into those free places, so the load counts never change;
+    //   3. read sub-step 0 of step kb + 1, so its LDS latency hides behind the MFMAs of the
+    //      last sub-step of step kb (the waves leave the barrier together).
     auto step = [&](auto S8_, int kb) {
       constexpr int S8 = decltype(S8_)::value, S = S8 & 3, P = S8 >> 2;
-      constexpr int kWait = kGroup ? 2 + (S == 1 ? kGroupLoads : 0) : kLoadsPerStep;
-      gemm_wait_vmcnt<kWait>();
-      asm volatile("s_barrier" ::: "memory");
-      const int kn = min(kb + 2, nk - 1);
-      if constexpr (kGroup) {
-        if constexpr (S == 0) load_group(gr[P ^ 1], min((kb >> 2) + 1, (nk >> 2) - 1));
-      } else {
-        load_codes(fr[(S + 2) & 3], kn);
-      }
-      dma_a(std::integral_constant<int, (S + 2) & 3>{}, kn);
-      __builtin_amdgcn_sched_barrier(0);
+      constexpr int kWait = 2 + (kGroup && S == 1 ? kGroupLoads : 0);
       const uint8_t* st = stage_ptr(std::integral_constant<int, S>{});
+      const uint8_t* sn = stage_ptr(std::integral_constant<int, (S + 1) & 3>{});
       const uint32_t* fw[NCT];
       typename F::Tab tab[NCT];
 #pragma unroll
@@ -279,15 +278,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
           tab[c] = F::table32(fr[S][c].s);
         }
       }
-      u32x4 av[2][4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) av[0][m] = *reinterpret_cast<const u32x4*>(st + apos[0] + 4096 * m);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         if (kk + 1 < 4) {
 #pragma unroll
           for (int m = 0; m < 4; ++m)
             av[(kk + 1) & 1][m] = *reinterpret_cast<const u32x4*>(st + apos[kk + 1] + 4096 * m);
+        } else {
+          __builtin_amdgcn_sched_barrier(0);
+          gemm_wait_vmcnt<kWait>();
+          asm volatile("s_barrier" ::: "memory");
+          if constexpr (kGroup) {
+            if constexpr (S == 0) load_group(gr[P ^ 1], min((kb >> 2) + 1, (nk >> 2) - 1));
+          } else {
+            load_codes(fr[(S + 2) & 3], min(kb + 2, nk - 1));
+          }
+          dma_a(std::integral_constant<int, (S + 3) & 3>{}, min(kb + 3, nk - 1));
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int m = 0; m < 4; ++m) av[0][m] = *reinterpret_cast<const u32x4*>(sn + apos[0] + 4096 * m);
         }
 #pragma unroll
         for (int c = 0; c < NCT; ++c) {

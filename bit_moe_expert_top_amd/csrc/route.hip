@@ -8,7 +8,7 @@
 // high word and (2^32-1 - expert id) in the low word, so one unsigned max picks the largest
 // logit and, among equal logits, the lowest id.  k rounds of a wave max-reduction extract the
 // winners; lane j keeps the j-th winner.  Logits are read once, coalesced (lane l reads
-// columns l, l+64, ...).
+// columns l, l+64, ...), all of a lane's loads in flight together.
 #include "common.h"
 #include "kernels.h"
 
@@ -23,6 +23,33 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
+// Wave-wide maximum of a 64-bit key, the result in every lane.  Within each row of 16 lanes
+// four DPP exchanges (xor 1, xor 2, half-row mirror, row mirror) leave the row maximum in every
+// lane; the four row maxima are then read as scalars (v_readlane) and combined uniformly.
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = max_u64(v, dpp_u64<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = max_u64(v, dpp_u64<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = max_u64(v, dpp_u64<0x141>(v));  // row_half_mirror
+  v = max_u64(v, dpp_u64<0x140>(v));  // row_mirror
+  uint64_t m = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * r);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * r);
+    m = max_u64(m, ((uint64_t)hi << 32) | lo);
+  }
+  return m;
+}
+
 template <int VPL>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E,
                                                     int k, int32_t* __restrict__ ids,
@@ -31,23 +58,23 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* row = logits + (size_t)t * E;
+  // every load is issued before any is used (clamped index, no branch per load)
+  float lv[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) lv[i] = row[min(lane + kWave * i, E - 1)];
   uint64_t key[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int e = lane + kWave * i;
-    key[i] = 0;  // below every real key (no logit maps to an all-zero high word)
-    if (e < E) key[i] = ((uint64_t)order_key(row[e]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+    // 0 is below every real key (no logit maps to an all-zero high word)
+    key[i] = e < E ? ((uint64_t)order_key(lv[i]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e) : 0;
   }
   uint64_t mine = 0;
   for (int j = 0; j < k; ++j) {
     uint64_t best = key[0];
 #pragma unroll
-    for (int i = 1; i < VPL; ++i) best = key[i] > best ? key[i] : best;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      uint64_t o = __shfl_xor(best, off);
-      best = o > best ? o : best;
-    }
+    for (int i = 1; i < VPL; ++i) best = max_u64(best, key[i]);
+    best = wave_max_u64(best);
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
       if (key[i] == best) key[i] = 0;
