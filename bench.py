@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 GEMM_MIN_TOKENS = 128          # the library runs the grouped-GEMM kernels from this batch size
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, published
 METRIC = "MoE-layer tokens/sec + weight HBM GB/s (decode) / MFMA % (prefill)"
 CSRC = os.path.join(ROOT, "bit_moe_expert_top_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -71,12 +72,16 @@ def measured_traffic(workload: str):
     return None
 
 
-def weight_bytes_per_expert(sp: dict, which: int) -> int:
-    """Packed bytes (codes + scales) of one expert's W1 (which=1) or W2 (which=2)."""
+def weight_bytes_per_expert(sp: dict, which: int, fmt: str | None = None) -> int:
+    """Packed bytes (codes + scales) of one expert's W1 (which=1) or W2 (which=2), in the
+    layer's low-bit format or in `fmt` ("w2", "w3", "mxfp4")."""
     H, I = sp["H"], sp["I"]
     n = 2 * I * H if which == 1 else H * I
-    if sp["fmt"] == "w2":
+    fmt = fmt or sp["fmt"]
+    if fmt == "w2":
         return n // 4 + (n // 32) * 2
+    if fmt == "mxfp4":
+        return n // 2 + n // 32
     return n * 3 // 8 + n // 64
 
 
@@ -221,17 +226,40 @@ def measure(sp: dict, dw, T: int, steps: int, warmup: int, flush_between: bool =
     stage_ms = [[e[1 + 2 * s].elapsed_time(e[2 + 2 * s]) for e in all_evs] for s in range(n_stages)]
     eager_ms = float(np.mean(step_ms))
     ms = float(np.mean(graph_ms)) if graph_ms else eager_ms
-    # low-bit stages: 1 FC1 streaming, 2 FC1 grouped GEMM, 3 FC2 streaming, 4 FC2 grouped GEMM
+    # low-bit stages: 1 FC1 streaming, 2 FC1 grouped GEMM, 3 FC2 streaming, 4 FC2 grouped GEMM;
+    # with a hot set: 5 hot prepare, then per batch of hot experts 3 stages (convert, FP8 FC1,
+    # FP8 FC2)
     fc1_ms = float(np.mean(stage_ms[1]) + np.mean(stage_ms[2]))
     fc2_ms = float(np.mean(stage_ms[3]) + np.mean(stage_ms[4]))
-    w1b = n_active * weight_bytes_per_expert(sp, 1)
-    w2b = n_active * weight_bytes_per_expert(sp, 2)
+    hot_batches = (n_stages - 6) // 3 if sp["n_hot"] > 0 else 0
+    conv_ms = sum(float(np.mean(stage_ms[6 + 3 * b])) for b in range(hot_batches))
+    hot_fc1_ms = sum(float(np.mean(stage_ms[7 + 3 * b])) for b in range(hot_batches))
+    hot_fc2_ms = sum(float(np.mean(stage_ms[8 + 3 * b])) for b in range(hot_batches))
+    hot = torch.zeros(E, dtype=torch.bool, device=dev)
+    if sp["n_hot"] > 0:
+        hot[torch.from_numpy(moegen.hot_ids(sp)).long().to(dev)] = True
+    n_hot_active = int(((counts > 0) & hot).sum().item())
+    n_cold_active = n_active - n_hot_active
+    hot_rows = int(counts[hot].sum().item())
+    w1b = n_cold_active * weight_bytes_per_expert(sp, 1) + n_hot_active * weight_bytes_per_expert(sp, 1, "mxfp4")
+    w2b = n_cold_active * weight_bytes_per_expert(sp, 2) + n_hot_active * weight_bytes_per_expert(sp, 2, "mxfp4")
     gemm = T >= GEMM_MIN_TOKENS
     workload = f"{sp['name']} MoE layer E={E} top-{k} H={H} I={I} {sp['fmt']} T={T}"
-    if gemm:
+    if sp["n_hot"] > 0:
+        workload += f" ({sp['n_hot']} hot experts mxfp4->fp8)"
+    if hot_batches > 0 and hot_rows > 0:
+        # hot experts carry most rows: their FP8 FC1 (+ SwiGLU + MXFP8 of h) is the dominant
+        # kernel; algorithmic flops = 2 * rows * (2I) * H over the hot experts' rows
+        f = 2.0 * hot_rows * (2 * I) * H
+        roof_ms = hot_fc1_ms / hot_batches
+        achieved = f / hot_batches / (roof_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": "moe_expert_ffn hot FP8 FC1 + SwiGLU + MXFP8 of h (fp8_gemm_kernel<1>)",
+                "achieved": achieved, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / FP8_PEAK_TFLOPS, "alg_flops_per_launch": f / hot_batches, "hot_rows": hot_rows}
+    elif gemm:
         # prefill-sized: FC1 of the groups above 32 rows is the grouped GEMM (stage 2);
         # algorithmic flops = 2 * rows * (2I) * H over the rows of those groups
-        gemm_rows = int(counts[counts > 32].sum().item())
+        gemm_rows = int(counts[(counts > 32) & ~hot].sum().item())
         fc1_flops = 2.0 * gemm_rows * (2 * I) * H
         roof_ms = float(np.mean(stage_ms[2]))
         achieved = fc1_flops / (roof_ms * 1e-3) / 1e12
@@ -268,10 +296,11 @@ def measure(sp: dict, dw, T: int, steps: int, warmup: int, flush_between: bool =
         "roofline": roof,
         "step_timing": "HIP graph replay" if graph_ms else "eager launches",
         "ms_per_step_eager": eager_ms,
-        "stages_ms": {"route+permute+prepare+combine (eager)": eager_ms - fc1_ms - fc2_ms, "fc1": fc1_ms, "fc2": fc2_ms},
+        "stages_ms": {"route+permute+prepare+combine (eager)": eager_ms - fc1_ms - fc2_ms - conv_ms - hot_fc1_ms - hot_fc2_ms,
+                      "fc1": fc1_ms, "fc2": fc2_ms, "hot_convert": conv_ms, "hot_fc1": hot_fc1_ms, "hot_fc2": hot_fc2_ms},
         "ffn_stage_ms": [float(np.mean(v)) for v in stage_ms],
-        "weight_GBps_fc1_fc2": (w1b + w2b) / ((fc1_ms + fc2_ms) * 1e-3) / 1e9,
-        "ffn_TFLOPs_fc1_fc2": all_flops / ((fc1_ms + fc2_ms) * 1e-3) / 1e12,
+        "weight_GBps_fc1_fc2": (w1b + w2b) / ((fc1_ms + fc2_ms + hot_fc1_ms + hot_fc2_ms) * 1e-3) / 1e9,
+        "ffn_TFLOPs_fc1_fc2": all_flops / ((fc1_ms + fc2_ms + hot_fc1_ms + hot_fc2_ms) * 1e-3) / 1e12,
         "ms_per_step_min": float(np.min(graph_ms or step_ms)),
         "ms_per_step_median": float(np.median(graph_ms or step_ms)),
         "wall_s_timed_loop_incl_flush": wall,
@@ -298,7 +327,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--layer", default="decode", help="decode | tiny")
+    ap.add_argument("--layer", default="decode", help="decode | prefill | mixed | w3 | tiny")
     ap.add_argument("--T", type=int, default=64)
     ap.add_argument("--no-flush", action="store_true", help="do not flush caches between steps")
     ap.add_argument("--cpu-tokens", type=int, default=64, help="tokens of the oracle's timed sample (0 = skip)")
@@ -307,7 +336,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this MoE layer path runs on one GPU; --gpus above 1 is not supported "
-              "(the multi-GPU split is described in DESIGN.md, not built)", file=sys.stderr)
+              "(an expert-parallel split over several GPUs is not built)", file=sys.stderr)
         sys.exit(2)
     sp, dw = setup_layer(args.layer)
     res = measure(sp, dw, args.T, args.steps, args.warmup, not args.no_flush)

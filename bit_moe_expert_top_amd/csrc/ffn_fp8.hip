@@ -302,7 +302,11 @@ __global__ __launch_bounds__(256, 2) void fp8_gemm_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);  // the store of step kb + 1 after this step's MFMAs
       if (kb + 1 < nk) store_step(stg[P ^ 1], P ^ 1);
-      __syncthreads();
+      // LDS writes done, then a bare barrier: step kb + 1 is in LDS for every wave and every wave
+      // is done with buffer P.  (A __syncthreads fence would also drain the loads of step kb + 2
+      // issued above, which are only needed at the end of the next step.)
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt not waited on
+      asm volatile("s_barrier" ::: "memory");
     };
 
     load_step(stg[0], 0);
