@@ -156,3 +156,14 @@ def batch(sp: dict, T: int) -> dict:
         logits = (z - pen[None, :]).astype(np.float32)
     x = _f32_to_bf16_bits(r.standard_normal((T, sp["H"]), dtype=np.float32))
     return dict(logits=np.ascontiguousarray(logits), x=x)
+
+
+def float_weights(rows: int, K: int, seed: int, spread: bool = True) -> np.ndarray:
+    """Seeded fp32 float weights ``[rows][K]`` standing in for a trained expert matrix that is
+    about to be quantised: N(0, 0.02^2), each row scaled by a factor 2^U(-3, 3) when `spread`
+    (rows of different magnitude, as in real layers).  Random draws only."""
+    r = _rng(2000, seed, rows, K)
+    w = r.standard_normal((rows, K)) * 0.02
+    if spread:
+        w = w * np.exp2(r.uniform(-3.0, 3.0, size=(rows, 1)))
+    return w.astype(np.float32)
