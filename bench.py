@@ -307,6 +307,51 @@ def measure(sp: dict, dw, T: int, steps: int, warmup: int, flush_between: bool =
     }
 
 
+def measure_quantize(steps: int, warmup: int, flush_between: bool = True) -> dict:
+    """Time the quantisers (fp32 weights -> 2-bit codebook, -> MXFP4) on the W1 matrices of 8
+    experts of the decode/prefill shape: [8 * 4096][4096] fp32 (512 MiB), resident in HBM.
+    Both kernels read each weight once: bound = HBM, algorithmic bytes = 4 per weight in plus
+    the packed bytes out."""
+    import numpy as np
+    import torch
+
+    from bit_moe_expert_top_amd import _lib as L
+
+    rows, K = 8 * 4096, 4096
+    n = rows * K
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2024)
+    w = torch.randn((rows, K), generator=g, device="cuda", dtype=torch.float32) * 0.02
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, f, out_b in (("w2", L.moe_quantize_w2, 2.0 / 8 + 2.0 / 32), ("mxfp4", L.moe_quantize_mxfp4, 0.5 + 1.0 / 32)):
+        for _ in range(warmup):
+            f(w)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in evs:
+            if flush_between:
+                flush.sum()
+            a.record(stream)
+            f(w)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        res[name] = {"ms": ms, "weights_per_s": n / (ms * 1e-3), "GBps": n * (4 + out_b) / (ms * 1e-3) / 1e9}
+    r = res["w2"]
+    return {
+        "metric": "quantiser weights/s (fp32 -> 2-bit codebook + bf16 group-32 scales)",
+        "value": r["weights_per_s"], "unit": "weights/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": r["ms"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic (N(0, 0.02^2) fp32 weights, seeded torch generator)",
+        "config": {"workload": f"quantise W1 of 8 experts: f32[{rows}][{K}]", "cache_flush_between_steps": flush_between},
+        "roofline": {"bound": "hbm", "kernel": "quantize_w2_kernel", "achieved": r["GBps"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": r["GBps"] / HBM_PEAK_GBS, "traffic": None, "avg_launch_ms": r["ms"]},
+        "mxfp4": res["mxfp4"],
+    }
+
+
 def copy_calibration(mib: int):
     """A plain device copy of known size (mib MiB read, mib MiB written), run after the timed
     region so that one counter run sees both it and the timed kernels: FETCH_SIZE and
@@ -327,7 +372,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--layer", default="decode", help="decode | prefill | mixed | w3 | tiny")
+    ap.add_argument("--layer", default="decode", help="decode | prefill | mixed | w3 | tiny | quantize (the quantisers, not a layer)")
     ap.add_argument("--T", type=int, default=64)
     ap.add_argument("--no-flush", action="store_true", help="do not flush caches between steps")
     ap.add_argument("--cpu-tokens", type=int, default=64, help="tokens of the oracle's timed sample (0 = skip)")
@@ -338,6 +383,9 @@ def main():
         print("bench.py: this MoE layer path runs on one GPU; --gpus above 1 is not supported "
               "(an expert-parallel split over several GPUs is not built)", file=sys.stderr)
         sys.exit(2)
+    if args.layer == "quantize":
+        print(json.dumps(measure_quantize(args.steps, args.warmup, not args.no_flush)), flush=True)
+        return
     sp, dw = setup_layer(args.layer)
     res = measure(sp, dw, args.T, args.steps, args.warmup, not args.no_flush)
     if args.copy_calib_mib > 0:

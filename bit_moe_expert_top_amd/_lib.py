@@ -47,6 +47,8 @@ _SIGS = {
     "moe_combine": (_i32, [_p, _p, _p, _i32, _i32, _i32, _p, _i32, _p]),
     "moe_mxfp4_to_fp8": (_i32, [_p, _p, _i64, _i32, _p, _p, _p]),
     "moe_mxfp8_quantize": (_i32, [_p, _i64, _i32, _p, _p, _p]),
+    "moe_quantize_w2": (_i32, [_p, _i64, _i32, _p, _p, _p]),
+    "moe_quantize_mxfp4": (_i32, [_p, _i64, _i32, _p, _p, _p]),
     "moe_debug_dequant": (_i32, [ctypes.POINTER(MoeWeights), _i32, _i32, _p, _p]),
     "moe_status_str": (ctypes.c_char_p, [_i32]),
 }
@@ -194,6 +196,24 @@ def moe_mxfp8_quantize(x: torch.Tensor):
     sc = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device)
     _check("moe_mxfp8_quantize", lib.moe_mxfp8_quantize(_ptr(x), rows, K, _ptr(elems), _ptr(sc), _stream()))
     return elems, sc
+
+
+def moe_quantize_w2(w: torch.Tensor):
+    """fp32 [rows][K] (device) -> (codes int32 [rows][K/16], bf16 scale bits int16 [rows][K/32])."""
+    rows, K = w.shape
+    codes = torch.empty((rows, K // 16), dtype=torch.int32, device=w.device)
+    sc = torch.empty((rows, K // 32), dtype=torch.int16, device=w.device)
+    _check("moe_quantize_w2", lib.moe_quantize_w2(_ptr(w), rows, K, _ptr(codes), _ptr(sc), _stream()))
+    return codes, sc
+
+
+def moe_quantize_mxfp4(w: torch.Tensor):
+    """fp32 [rows][K] (device) -> (codes uint8 [rows][K/2], e8m0 scales uint8 [rows][K/32])."""
+    rows, K = w.shape
+    codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=w.device)
+    sc = torch.empty((rows, K // 32), dtype=torch.uint8, device=w.device)
+    _check("moe_quantize_mxfp4", lib.moe_quantize_mxfp4(_ptr(w), rows, K, _ptr(codes), _ptr(sc), _stream()))
+    return codes, sc
 
 
 def moe_debug_dequant(w: DeviceWeights, e: int, which: int):

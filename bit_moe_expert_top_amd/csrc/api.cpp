@@ -323,6 +323,22 @@ moe_status moe_mxfp8_quantize(const uint16_t* x, int64_t rows, int32_t K, uint8_
   return from_hip(launch_mxfp8_quantize(x, rows, K, elems, scales, as_stream(stream)));
 }
 
+moe_status moe_quantize_w2(const float* w, int64_t rows, int32_t K, uint32_t* codes, uint16_t* scales,
+                           void* stream) {
+  if (rows < 0 || K <= 0 || K % 32) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (!w || !codes || !scales) return MOE_ERR_INVALID_ARG;
+  return from_hip(launch_quantize_w2(w, rows, K, codes, scales, as_stream(stream)));
+}
+
+moe_status moe_quantize_mxfp4(const float* w, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
+                              void* stream) {
+  if (rows < 0 || K <= 0 || K % 32) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (!w || !codes || !scales) return MOE_ERR_INVALID_ARG;
+  return from_hip(launch_quantize_mxfp4(w, rows, K, codes, scales, as_stream(stream)));
+}
+
 moe_status moe_debug_dequant(const moe_weights* w, int32_t e, int32_t which, float* out,
                              void* stream) {
   moe_status st = check_weights(w);

@@ -179,7 +179,7 @@ __global__ __launch_bounds__(256, 2) void fp8_gemm_kernel(
     int ktop, const uint8_t* __restrict__ asrc, const uint8_t* __restrict__ ascale,
     const int32_t* __restrict__ perm, int64_t a_rows, void* __restrict__ out,
     uint8_t* __restrict__ out_scale) {
-  extern __shared__ __align__(16) uint8_t lds8[];
+  __shared__ __align__(16) uint8_t lds8[kF8Lds];  // static: gfx950 has 160 KB of LDS per CU
   const int tid = threadIdx.x, lane = wave_lane(), w = tid / kWave;
   const int wm = w & 1, wn = w >> 1, hl = lane >> 5, r32 = lane & 31;
   const int n_items = plan[0];
@@ -386,16 +386,9 @@ static hipError_t launch_fp8(const int32_t* plan, int b0, int S, const uint8_t* 
                              const uint8_t* asrc, const uint8_t* ascale, const int32_t* perm,
                              int64_t a_rows, int64_t tasks, void* out, uint8_t* out_scale,
                              hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)fp8_gemm_kernel<FC>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kF8Lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   const int64_t cap = 256 * 2;
   const int grid = (int)(tasks < cap ? (tasks > 0 ? tasks : 1) : cap);
-  fp8_gemm_kernel<FC><<<grid, 256, kF8Lds, s>>>(plan, b0, S, slots, slot_bytes, w_off, ws_off, rows, K,
+  fp8_gemm_kernel<FC><<<grid, 256, 0, s>>>(plan, b0, S, slots, slot_bytes, w_off, ws_off, rows, K,
                                                 width, ktop, asrc, ascale, perm, a_rows, out, out_scale);
   return hipGetLastError();
 }

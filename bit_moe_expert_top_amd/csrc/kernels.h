@@ -79,6 +79,11 @@ hipError_t launch_mxfp8_quantize(const uint16_t* x, int64_t rows, int K, uint8_t
                                  uint8_t* scales, hipStream_t s);
 hipError_t launch_mxfp4_to_fp8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int K,
                                uint8_t* elems, uint8_t* out_scales, hipStream_t s);
+// Quantisers (quant.hip): fp32 [rows][K] -> 2-bit codes + bf16 scales, or MXFP4.
+hipError_t launch_quantize_w2(const float* w, int64_t rows, int K, uint32_t* codes, uint16_t* scales,
+                              hipStream_t s);
+hipError_t launch_quantize_mxfp4(const float* w, int64_t rows, int K, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t s);
 // Hot work list (items of <= chunk_rows rows of hot experts) and MXFP8 of x, in one launch.
 hipError_t launch_hot_prepare(const int32_t* offsets, int E, int chunk_rows, const int32_t* hot_ids,
                               int n_hot, int32_t* plan, const uint16_t* x, int T, int H, uint8_t* xq,

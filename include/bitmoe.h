@@ -183,6 +183,31 @@ moe_status moe_mxfp4_to_fp8(const uint8_t* codes, const uint8_t* scales, int64_t
 moe_status moe_mxfp8_quantize(const uint16_t* x, int64_t rows, int32_t K, uint8_t* elems,
                               uint8_t* scales, void* stream);
 
+/* moe_quantize_w2 -- fit fp32 weights to the 2-bit codebook format ([Moet-QA]: 2-bit experts on
+ * the codebook {-4,-1,1,4}; the pages do not give the fitting procedure).  Per group of 32
+ * consecutive weights along K of one row: the least-squares fit w ~ level[code] * s by
+ * alternating nearest-level codes and the scale sum(level*w)/sum(level^2), from
+ * s = max|w|/4, three rounds, then s rounded to bf16 (nearest even) and the final codes
+ * chosen against that stored scale.  All decisions in fp32 in a fixed order (deterministic);
+ * nearest-level rule with t = 2.5 s: +4 if w > t, +1 if 0 <= w <= t, -1 if -t <= w < 0,
+ * -4 if w < -t.  An all-zero group gets scale 0 and code 2 (+1).
+ *   w f32[rows][K] (finite) -> codes u32[rows][K/16] (code i of a word at bits [2i, 2i+2)),
+ *   scales u16[rows][K/32] (bf16 bits).  The output is the MOE_FMT_W2_CB4_G32_BF16 layout of
+ *   one weight matrix (W1 of an expert is [2I][H], W2 is [H][I]).
+ * Errors: INVALID_ARG (rows < 0, K not a positive multiple of 32, null pointer with rows > 0). */
+moe_status moe_quantize_w2(const float* w, int64_t rows, int32_t K, uint32_t* codes, uint16_t* scales,
+                           void* stream);
+
+/* moe_quantize_mxfp4 -- [OCP-MX] MXFP4 quantisation of fp32 weights, blocks of 32 along K:
+ * shared exponent floor(log2(amax)) - 2, clamped to [-127, 127] (scale byte 0 for an all-zero
+ * block); elements w / 2^shared rounded to the nearest e2m1 value, ties to the even mantissa,
+ * saturating at +-6; the sign of -0 is kept.
+ *   w f32[rows][K] (finite) -> codes u8[rows][K/2] (element 2i in the low nibble),
+ *   scales u8[rows][K/32] (e8m0) -- the MOE_FMT_MXFP4 layout.
+ * Errors: INVALID_ARG as moe_quantize_w2. */
+moe_status moe_quantize_mxfp4(const float* w, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
+                              void* stream);
+
 /* moe_debug_dequant -- decode one low-bit expert matrix with the same device code the FFN
  * kernels use, into f32[rows][K] (W1: rows = 2I, K = H; W2: rows = H, K = I), in natural K
  * order.  For tests: the decoded weights must equal the format definition bit for bit.

@@ -95,3 +95,17 @@ def test_ffn_rejects_batches_beyond_32bit_offsets(lib):
     T = (1 << 32) // (4096 * 2)  # T * H * 2 == 2^32
     assert L.lib.moe_expert_ffn(ctypes.byref(w), p, T, 1, p, p, p, p, p, 1 << 40, None) == -2
     assert L.lib.moe_expert_ffn(ctypes.byref(w), p, T - 1, 1, p, p, p, p, p, 10, None) == -3  # ws check next
+
+
+def test_quantizer_argument_checks(lib):
+    p = ctypes.c_void_p(16)
+    for name in ("moe_quantize_w2", "moe_quantize_mxfp4"):
+        f = getattr(lib, name)
+        f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                      ctypes.c_void_p]
+        assert f(p, 4, 48, p, p, None) == -1      # K not a multiple of 32
+        assert f(p, 4, 0, p, p, None) == -1       # K <= 0
+        assert f(p, -1, 64, p, p, None) == -1     # rows < 0
+        assert f(None, 4, 64, p, p, None) == -1   # null input
+        assert f(p, 4, 64, p, None, None) == -1   # null output
+        assert f(None, 0, 64, None, None, None) == 0  # rows = 0 is a no-op
