@@ -181,6 +181,7 @@ __global__ __launch_bounds__(256, 2) void fp8_gemm_kernel(
     uint8_t* __restrict__ out_scale) {
   __shared__ __align__(16) uint8_t lds8[kF8Lds];  // static: gfx950 has 160 KB of LDS per CU
   const int tid = threadIdx.x, lane = wave_lane(), w = tid / kWave;
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // the wave index as a uniform value
   const int wm = w & 1, wn = w >> 1, hl = lane >> 5, r32 = lane & 31;
   const int n_items = plan[0];
   const int4* items = reinterpret_cast<const int4*>(plan + 4);
@@ -246,7 +247,10 @@ __global__ __launch_bounds__(256, 2) void fp8_gemm_kernel(
         g.a[u] = buf_load16(ra, aoff[u] + ko);
         g.b[u] = buf_load16(rb, boff[u] + ko);
       }
-      g.s = tid < 128 ? buf_load4(ras, asoff + 4u * kb) : buf_load4(rbs, bsoff + 4u * kb);
+      // waves 0, 1 (threads 0..127) load the A scales, waves 2, 3 the B scales: the resource is
+      // chosen per wave (a per-lane choice of resource makes the compiler loop over both)
+      const bool a_side = wu < 2;
+      g.s = buf_load4(a_side ? ras : rbs, (a_side ? asoff : bsoff) + 4u * kb);
     };
     auto store_step = [&](const Staged& g, int buf) {
       uint8_t* la = lds8 + buf * kF8Buf;
@@ -301,7 +305,7 @@ __global__ __launch_bounds__(256, 2) void fp8_gemm_kernel(
           for (int b = 0; b < 2; ++b) acc[a][b] = mfma_scale_32x32x64_fp8(av[a], bv[b], acc[a][b], sa[a], sbv[b]);
       }
       __builtin_amdgcn_sched_barrier(0);  // the store of step kb + 1 after this step's MFMAs
-      if (kb + 1 < nk) store_step(stg[P ^ 1], P ^ 1);
+      store_step(stg[P ^ 1], P ^ 1);  // unconditional (at the last step: a clamped reload, unused)
       // LDS writes done, then a bare barrier: step kb + 1 is in LDS for every wave and every wave
       // is done with buffer P.  (A __syncthreads fence would also drain the loads of step kb + 2
       // issued above, which are only needed at the end of the next step.)
