@@ -93,3 +93,35 @@ def test_quantize_empty(L):
     for f in (L.moe_quantize_w2, L.moe_quantize_mxfp4):
         c, s = f(torch.empty((0, 64), dtype=torch.float32, device="cuda"))
         assert c.numel() == 0 and s.numel() == 0
+
+
+def test_quantised_layer_end_to_end(L):
+    """Float experts -> GPU quantiser -> the four calls, against the oracle on the same seeded
+    float weights: the quantised codes and scales equal the oracle's bit for bit, and the layer
+    on them is within the bf16 tolerance of the oracle layer on the oracle's codes."""
+    from oracle import moe as OM
+    from _helpers import TOL_BF16, max_err_over_rms
+
+    E, k, H, I, T = 8, 2, 256, 512, 40
+    w1 = np.stack([moegen.float_weights(2 * I, H, 100 + e) for e in range(E)])
+    w2 = np.stack([moegen.float_weights(H, I, 200 + e) for e in range(E)])
+    c1, s1 = L.moe_quantize_w2(torch.from_numpy(w1.reshape(E * 2 * I, H)).cuda())
+    c2, s2 = L.moe_quantize_w2(torch.from_numpy(w2.reshape(E * H, I)).cuda())
+    torch.cuda.synchronize()
+    arrays = {"w1_codes": host(c1).view(np.uint32).reshape(E, 2 * I, H // 16),
+              "w1_scales": host(s1).view(np.uint16).reshape(E, 2 * I, H // 32),
+              "w2_codes": host(c2).view(np.uint32).reshape(E, H, I // 16),
+              "w2_scales": host(s2).view(np.uint16).reshape(E, H, I // 32)}
+    oc1, os1 = OQ.quantize_w2(w1.reshape(E * 2 * I, H))
+    oc2, os2 = OQ.quantize_w2(w2.reshape(E * H, I))
+    assert np.array_equal(arrays["w1_codes"].reshape(oc1.shape), oc1)
+    assert np.array_equal(arrays["w1_scales"].reshape(os1.shape), os1)
+    assert np.array_equal(arrays["w2_codes"].reshape(oc2.shape), oc2)
+    assert np.array_equal(arrays["w2_scales"].reshape(os2.shape), os2)
+    dw = L.DeviceWeights(1, E, H, I, arrays)
+    sp = moegen.spec("tiny")
+    b = moegen.batch(sp, T)
+    res = L.layer_forward(dw, torch.from_numpy(b["logits"]).cuda(),
+                          torch.from_numpy(b["x"].view(np.int16)).cuda(), k, out_fp32=True)
+    want = OM.layer_forward(OM.Layer("w2", arrays), b["logits"], b["x"], k)
+    assert max_err_over_rms(host(res["out"]), want["out"]) <= TOL_BF16
