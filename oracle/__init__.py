@@ -2,7 +2,9 @@
 
 Plain, slow, obviously correct numpy (fp64) definitions of every step of the layer:
 routing, grouping, low-bit dequantisation, MXFP4 -> FP8 conversion, MXFP8 activation
-quantisation, the SwiGLU expert FFN and the gate-weighted combine.  Only ``tests/``,
+quantisation, the SwiGLU expert FFN and the gate-weighted combine; and of the quantisers that
+produce the low-bit formats from fp32 weights (``quant``: decisions taken in fp32, in a fixed
+order, so that a GPU quantiser can match them bit for bit).  Only ``tests/``,
 ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may import it;
 the HIP library never does, and this package imports nothing from it (no shared code,
 tables or constants).
@@ -27,4 +29,4 @@ Readings taken where the pages are silent or ambiguous are stated next to the co
 that takes them.  Every function here is pinned by tests in ``tests/test_oracle_*.py``
 against worked examples, brute force, closed forms or invariants.
 """
-from . import formats, moe  # noqa: F401
+from . import formats, moe, quant  # noqa: F401
