@@ -152,6 +152,21 @@ hipError_t launch_mxfp4_to_fp8(const uint8_t* codes, const uint8_t* scales, int6
   return hipGetLastError();
 }
 
+// Maximum over the 32 lanes of each half-wave, in every lane: DPP exchanges within rows of 16
+// (xor 1, xor 2, half-row mirror, row mirror), then one ds_swizzle across the two rows of the
+// half-wave (bit mode: xor 16) -- instead of five ds_bpermute round trips.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t half_wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = max(v, dpp_u32<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = max(v, dpp_u32<0x141>(v));  // row_half_mirror
+  v = max(v, dpp_u32<0x140>(v));  // row_mirror
+  return max(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (0x10 << 10) | 0x1F));
+}
+
 // ------------------------------------------------------------------ FP8 grouped GEMM
 constexpr int kF8BM = 128, kF8BN = 128, kF8BK = 128;
 constexpr int kF8Row = kF8BK + 16;                  // LDS bytes per tile row (16 B of padding)
@@ -334,8 +349,7 @@ __global__ __launch_bounds__(256, 2) void fp8_gemm_kernel(
           const uint32_t hb = __float_as_uint(hv);
           // MXFP8 over the 32 columns of this row held by the 32 lanes of this half-wave
           uint32_t m = hb & 0x7FFFFFFFu;
-#pragma unroll
-          for (int off = 1; off < 32; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+          m = half_wave_max_u32(m);
           const int shared = mx_shared_exp(m ? floor_log2_f32(m) : 0, m == 0);
           const uint32_t e = f32_to_e4m3_scaled(hb, shared);
           if (row < nrows) {
