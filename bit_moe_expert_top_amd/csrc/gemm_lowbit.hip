@@ -347,7 +347,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
         }
       }
     }
-    __syncthreads();  // every wave is done with the token stages before the next tile fills them
+    // every wave is done reading the token stages before the next tile fills them: an LDS-only
+    // wait and a bare barrier (a __syncthreads fence would also wait for this tile's h / y
+    // stores, which nothing in this workgroup reads)
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt not waited on
+    asm volatile("s_barrier" ::: "memory");
   }
 }
 
