@@ -131,7 +131,8 @@ def setup_layer(name: str):
     return sp, dw
 
 
-def measure(sp: dict, dw, T: int, steps: int, warmup: int, flush_between: bool = True) -> dict:
+def measure(sp: dict, dw, T: int, steps: int, warmup: int, flush_between: bool = True,
+            batch_invariant: bool = False) -> dict:
     """Time `steps` layer steps on T tokens; returns the bench record (without cpu_baseline)."""
     import numpy as np
     import torch
@@ -243,10 +244,12 @@ def measure(sp: dict, dw, T: int, steps: int, warmup: int, flush_between: bool =
     hot_rows = int(counts[hot].sum().item())
     w1b = n_cold_active * weight_bytes_per_expert(sp, 1) + n_hot_active * weight_bytes_per_expert(sp, 1, "mxfp4")
     w2b = n_cold_active * weight_bytes_per_expert(sp, 2) + n_hot_active * weight_bytes_per_expert(sp, 2, "mxfp4")
-    gemm = T >= GEMM_MIN_TOKENS
+    gemm = T >= GEMM_MIN_TOKENS and not batch_invariant  # the invariant mode streams every group
     workload = f"{sp['name']} MoE layer E={E} top-{k} H={H} I={I} {sp['fmt']} T={T}"
     if sp["n_hot"] > 0:
         workload += f" ({sp['n_hot']} hot experts mxfp4->fp8)"
+    if batch_invariant:
+        workload += " batch-invariant mode"
     if hot_batches > 0 and hot_rows > 0:
         # hot experts carry most rows: their FP8 FC1 (+ SwiGLU + MXFP8 of h) is the dominant
         # kernel; algorithmic flops = 2 * rows * (2I) * H over the hot experts' rows
@@ -292,7 +295,7 @@ def measure(sp: dict, dw, T: int, steps: int, warmup: int, flush_between: bool =
         "dtype": "bf16",
         "data": f"synthetic (seeded; uniform {sp['fmt']} codes and scales, N(0,1) bf16 x, Zipf s=1.1 router logits)",
         "config": {"workload": workload, "tokens": T, "experts_active": n_active,
-                   "cache_flush_between_steps": flush_between},
+                   "cache_flush_between_steps": flush_between, "batch_invariant": batch_invariant},
         "roofline": roof,
         "step_timing": "HIP graph replay" if graph_ms else "eager launches",
         "ms_per_step_eager": eager_ms,
@@ -375,6 +378,8 @@ def main():
     ap.add_argument("--layer", default="decode", help="decode | prefill | mixed | w3 | tiny | quantize (the quantisers, not a layer)")
     ap.add_argument("--T", type=int, default=64)
     ap.add_argument("--no-flush", action="store_true", help="do not flush caches between steps")
+    ap.add_argument("--batch-invariant", action="store_true",
+                    help="run the layer in its batch-invariant mode (same bits for a token at any T)")
     ap.add_argument("--cpu-tokens", type=int, default=64, help="tokens of the oracle's timed sample (0 = skip)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after timing, run a plain copy of this many MiB (counter calibration)")
@@ -387,7 +392,8 @@ def main():
         print(json.dumps(measure_quantize(args.steps, args.warmup, not args.no_flush)), flush=True)
         return
     sp, dw = setup_layer(args.layer)
-    res = measure(sp, dw, args.T, args.steps, args.warmup, not args.no_flush)
+    dw.set_batch_invariant(args.batch_invariant)
+    res = measure(sp, dw, args.T, args.steps, args.warmup, not args.no_flush, args.batch_invariant)
     if args.copy_calib_mib > 0:
         copy_calibration(args.copy_calib_mib)
     if args.cpu_tokens > 0:

@@ -32,7 +32,11 @@ class MoeWeights(ctypes.Structure):
         ("w1_codes", _p), ("w1_scales", _p), ("w2_codes", _p), ("w2_scales", _p),
         ("n_hot", _i32), ("hot_ids", _p),
         ("hot_w1_codes", _p), ("hot_w1_scales", _p), ("hot_w2_codes", _p), ("hot_w2_scales", _p),
+        ("flags", _i32),
     ]
+
+
+MOE_FLAG_BATCH_INVARIANT = 1
 
 
 _SIGS = {
@@ -87,7 +91,7 @@ class DeviceWeights:
     """Device copies of one layer's packed experts and the ``moe_weights`` struct that points
     at them (the tensors are kept alive by this object)."""
 
-    def __init__(self, fmt: int, E: int, H: int, I: int, arrays: dict, device="cuda"):
+    def __init__(self, fmt: int, E: int, H: int, I: int, arrays: dict, device="cuda", flags: int = 0):
         def t(a):
             return torch.from_numpy(a.view(_np_uint_as_int(a.dtype))).to(device) if a is not None else None
 
@@ -98,7 +102,12 @@ class DeviceWeights:
         g = lambda key: _ptr(self.t.get(key))
         self.c = MoeWeights(E, H, I, fmt, g("w1_codes"), g("w1_scales"), g("w2_codes"), g("w2_scales"),
                             self.n_hot, g("hot_ids"), g("hot_w1_codes"), g("hot_w1_scales"),
-                            g("hot_w2_codes"), g("hot_w2_scales"))
+                            g("hot_w2_codes"), g("hot_w2_scales"), flags)
+
+    def set_batch_invariant(self, on: bool = True):
+        """Switch the layer's batch-invariant mode (MOE_FLAG_BATCH_INVARIANT) on or off."""
+        self.c.flags = (self.c.flags | MOE_FLAG_BATCH_INVARIANT) if on else (self.c.flags & ~MOE_FLAG_BATCH_INVARIANT)
+        return self
 
 
 def _np_uint_as_int(dt):

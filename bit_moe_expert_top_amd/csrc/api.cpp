@@ -24,10 +24,18 @@ inline moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE
 // tile per K part.  (With distinct experts per token a group never exceeds T rows; repeated
 // ids can make it larger.)
 constexpr int kStreamChunk = 32;
-inline int stream_chunk(int T) { return T <= 16 ? 16 : kStreamChunk; }
 // In batches of at least this many tokens, the groups larger than kStreamChunk rows run on the
 // grouped-GEMM kernels (items of kGemmRows rows); smaller groups always stream.
 constexpr int kGemmMinTokens = 128;
+
+// Batch-invariant mode: every group streams, in items of 16 rows, and the streaming kernels
+// take the K split of a one-token batch (it then depends on H and I only).  A row's sums are
+// formed in the same order whatever T is: the kernels treat each token column on its own.
+inline bool invariant(const moe_weights* w) { return (w->flags & MOE_FLAG_BATCH_INVARIANT) != 0; }
+inline int stream_chunk(const moe_weights* w, int T) {
+  return (T <= 16 || invariant(w)) ? 16 : kStreamChunk;
+}
+inline int split_tokens(const moe_weights* w, int T) { return invariant(w) ? 1 : T; }
 
 // Hot experts are computed by the FP8 grouped GEMM on items of this many rows.
 constexpr int kHotChunk = 128;
@@ -46,9 +54,9 @@ struct FfnLayout {
 FfnLayout ffn_layout(const moe_weights* w, int T, int k) {
   FfnLayout L;
   const int64_t R = (int64_t)T * k;
-  L.gemm = T >= kGemmMinTokens;
+  L.gemm = T >= kGemmMinTokens && !invariant(w);
   const int64_t per_expert = R < w->E ? R : w->E;  // one partial item per expert at most
-  const int chunk = stream_chunk(T);
+  const int chunk = stream_chunk(w, T);
   L.max_items_s = (R + chunk - 1) / chunk + per_expert;
   L.max_items_g = L.gemm ? (R + kGemmRows - 1) / kGemmRows + per_expert : 0;
   size_t off = 0;
@@ -96,6 +104,7 @@ moe_status check_weights(const moe_weights* w) {
   if (w->fmt != MOE_FMT_W2 && w->fmt != MOE_FMT_W3) return MOE_ERR_INVALID_ARG;
   if (!w->w1_codes || !w->w1_scales || !w->w2_codes || !w->w2_scales) return MOE_ERR_INVALID_ARG;
   if (w->n_hot < 0 || w->n_hot > w->E) return MOE_ERR_INVALID_ARG;
+  if (w->flags & ~MOE_FLAG_BATCH_INVARIANT) return MOE_ERR_INVALID_ARG;
   if (w->n_hot > 0 && (!w->hot_ids || !w->hot_w1_codes || !w->hot_w1_scales || !w->hot_w2_codes ||
                        !w->hot_w2_scales))
     return MOE_ERR_INVALID_ARG;
@@ -226,17 +235,19 @@ moe_status ffn_run_stage(const moe_weights* w, const uint16_t* x, int32_t T, int
   hipError_t e = hipSuccess;
   switch (stage) {
     case 0:
-      e = launch_prepare(offsets, w->E, stream_chunk(T), kGemmRows, L.gemm, w->hot_ids, w->n_hot, plan_s, plan_g,
+      e = launch_prepare(offsets, w->E, stream_chunk(w, T), kGemmRows, L.gemm, w->hot_ids, w->n_hot, plan_s, plan_g,
                          x, T, w->H, lw.fmt, xp, s);
       break;
     case 1:
-      e = launch_lowbit_fc1(lw, w->E, w->H, w->I, k, xp, perm, plan_s, (int)L.max_items_s, T, hbuf, s);
+      e = launch_lowbit_fc1(lw, w->E, w->H, w->I, k, xp, perm, plan_s, (int)L.max_items_s, T,
+                            split_tokens(w, T), hbuf, s);
       break;
     case 2:
       if (L.gemm) e = launch_lowbit_gemm_fc1(lw, w->H, w->I, k, xp, perm, plan_g, (int)L.max_items_g, T, hbuf, s);
       break;
     case 3:
-      e = launch_lowbit_fc2(lw, w->E, w->H, w->I, k, hbuf, plan_s, (int)L.max_items_s, T, y_perm, s);
+      e = launch_lowbit_fc2(lw, w->E, w->H, w->I, k, hbuf, plan_s, (int)L.max_items_s, T,
+                            split_tokens(w, T), y_perm, s);
       break;
     case 4:
       if (L.gemm) e = launch_lowbit_gemm_fc2(lw, w->H, w->I, k, hbuf, plan_g, (int)L.max_items_g, T, y_perm, s);

@@ -419,9 +419,9 @@ static hipError_t launch_stream(const void* codes, const void* scales, int rows,
 
 hipError_t launch_lowbit_fc1(const LowbitWeights& w, int E, int H, int I, int k,
                              const uint16_t* xp, const int32_t* perm, const int32_t* plan,
-                             int max_items, int T, uint16_t* hbuf, hipStream_t s) {
+                             int max_items, int T, int split_T, uint16_t* hbuf, hipStream_t s) {
   (void)E;
-  const int ks = k_split_for(T, H);
+  const int ks = k_split_for(split_T, H);
   const int64_t tasks = (int64_t)max_items * ((I / 32) / (4 / ks));
   const uint32_t xb = (uint32_t)((size_t)T * H * 2);
   if (w.fmt == W2Fmt::kId)
@@ -433,9 +433,10 @@ hipError_t launch_lowbit_fc1(const LowbitWeights& w, int E, int H, int I, int k,
 
 hipError_t launch_lowbit_fc2(const LowbitWeights& w, int E, int H, int I, int k,
                              const uint16_t* hbuf, const int32_t* plan, int max_items, int T,
-                             float* y, hipStream_t s) {
+                             int split_T, float* y, hipStream_t s) {
   (void)E;
-  const int ks = k_split_for(T, I);
+  (void)T;
+  const int ks = k_split_for(split_T, I);
   const int64_t tasks = (int64_t)max_items * ((H / 64) / (4 / ks));
   const uint32_t hb = 0;  // unused: FC2 bases its resource at each item's rows
   if (w.fmt == W2Fmt::kId)

@@ -43,12 +43,14 @@ hipError_t launch_prepare(const int32_t* offsets, int E, int small_max, int gemm
                           const uint16_t* x, int T, int H, int fmt, uint16_t* xp, hipStream_t s);
 
 // Decode-style kernels: weight-streaming, MFMA on 16-token tiles.
+// split_T: the batch size the K split across a workgroup's waves is chosen for (T itself, or 1
+// for a split that does not depend on the batch)
 hipError_t launch_lowbit_fc1(const LowbitWeights& w, int E, int H, int I, int k,
                              const uint16_t* xp, const int32_t* perm, const int32_t* plan,
-                             int max_items, int T, uint16_t* hbuf, hipStream_t s);
+                             int max_items, int T, int split_T, uint16_t* hbuf, hipStream_t s);
 hipError_t launch_lowbit_fc2(const LowbitWeights& w, int E, int H, int I, int k,
                              const uint16_t* hbuf, const int32_t* plan, int max_items, int T,
-                             float* y, hipStream_t s);
+                             int split_T, float* y, hipStream_t s);
 
 // Prefill-sized groups: grouped GEMM on MFMA 32x32x16 with the codes decoded into LDS tiles.
 // Work items of at most kGemmRows rows.

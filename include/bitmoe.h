@@ -90,7 +90,19 @@ typedef struct {
   const void* hot_w1_scales;   /* [n_hot][2I][H/32] u8 e8m0                                  */
   const void* hot_w2_codes;    /* [n_hot][H][I/2]   u8                                       */
   const void* hot_w2_scales;   /* [n_hot][H][I/32]  u8 e8m0                                  */
+  int32_t flags;               /* 0 or MOE_FLAG_BATCH_INVARIANT; other bits: INVALID_ARG     */
 } moe_weights;
+
+/* [Moet-README] (results table of the DeepSeek-V4.1-Flash build, quality row): a request gives
+ * the same logits at any batch size.
+ * With this flag moe_expert_ffn computes every grouped row with one accumulation order that
+ * does not depend on T or on the other rows of the batch (the streaming kernels for every group,
+ * with one K split chosen from H and I alone), so a token's output has the same bits whatever
+ * batch it comes in.  Without it the K split follows T and large groups of large batches run on
+ * the grouped-GEMM kernels: faster, and the bits of a token may change with T (the values
+ * stay within the same tolerance of the exact result).  Routing, grouping, the FP8 hot path
+ * and the combine compute each token on its own in both modes. */
+#define MOE_FLAG_BATCH_INVARIANT 1
 
 /* moe_route -- top-k routing ([Moet-README]: each token is served by k routed experts).
  *   logits    f32[T][E]   router logits

@@ -85,6 +85,31 @@ def test_ffn_argument_checks(lib):
     assert L.lib.moe_debug_dequant(ctypes.byref(w), 8, 1, p, None) == -1  # expert out of range
 
 
+def test_ffn_flags(lib):
+    import sys
+    sys.path.insert(0, ROOT)
+    from bit_moe_expert_top_amd import _lib as L
+
+    p = 16
+    base = (8, 256, 512, L.MOE_FMT_W2, p, p, p, p, 0, None, None, None, None, None)
+    unknown = L.MoeWeights(*base, 2)
+    assert L.lib.moe_expert_ffn_ws_bytes(ctypes.byref(unknown), 256, 2, 0) == 0
+    assert L.lib.moe_expert_ffn(ctypes.byref(unknown), p, 16, 2, p, p, p, p, p, 1 << 30, None) == -1
+    plain = L.MoeWeights(*base, 0)
+    inv = L.MoeWeights(*base, L.MOE_FLAG_BATCH_INVARIANT)
+    # batch-invariant mode streams every group in 16-row items (no grouped-GEMM work list): the
+    # stream list is longer, the rest of the workspace the same
+    for T in (16, 256, 4096):
+        a = L.lib.moe_expert_ffn_ws_bytes(ctypes.byref(plain), T, 2, 0)
+        b = L.lib.moe_expert_ffn_ws_bytes(ctypes.byref(inv), T, 2, 0)
+        assert 0 < a and a <= b < a + 16 * 1024
+    assert L.lib.moe_expert_ffn_num_stages(ctypes.byref(inv), 256, 2, 1 << 30) == 5
+    dw = L.MoeWeights(*base)
+    assert dw.flags == 0
+    header = open(os.path.join(ROOT, "include", "bitmoe.h")).read()
+    assert "int32_t flags;" in header.split("} moe_weights;")[0].split("const void* hot_w2_scales;")[1]
+
+
 def test_ffn_rejects_batches_beyond_32bit_offsets(lib):
     import sys
     sys.path.insert(0, ROOT)
