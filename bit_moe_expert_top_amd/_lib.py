@@ -39,6 +39,11 @@ class MoeWeights(ctypes.Structure):
 MOE_FLAG_BATCH_INVARIANT = 1
 
 
+class MoeTierState(ctypes.Structure):
+    _fields_ = [("E", _i32), ("n_slots", _i32), ("slot_of_expert", _p), ("expert_of_slot", _p),
+                ("last_use", _p), ("tick", _i64)]
+
+
 _SIGS = {
     "moe_route": (_i32, [_p, _i32, _i32, _i32, _p, _p, _p]),
     "moe_permute_ws_bytes": (_sz, [_i32, _i32, _i32]),
@@ -55,6 +60,9 @@ _SIGS = {
     "moe_quantize_mxfp4": (_i32, [_p, _i64, _i32, _p, _p, _p]),
     "moe_debug_dequant": (_i32, [ctypes.POINTER(MoeWeights), _i32, _i32, _p, _p]),
     "moe_status_str": (ctypes.c_char_p, [_i32]),
+    "moe_tier_plan": (_i32, [ctypes.POINTER(MoeTierState), _p, _i64, _p, _p, _p]),
+    "moe_tier_load": (_i32, [ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeWeights), _p, _p, _i32, _p]),
+    "moe_tier_remap": (_i32, [_p, _i64, _p, _p, _p]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(lib, _name)
@@ -240,3 +248,96 @@ def layer_forward(w: DeviceWeights, logits: torch.Tensor, x: torch.Tensor, k: in
     y = moe_expert_ffn(w, x, k, counts, offsets, perm, fp8_slots=fp8_slots)
     out = moe_combine(y, inv, gw, out_fp32=out_fp32)
     return dict(ids=ids, gates=gw, counts=counts, offsets=offsets, perm=perm, inv=inv, y_perm=y, out=out)
+
+
+# --------------------------------------------------------------------- host-RAM expert tier
+class TierState:
+    """Host-side LRU slot state of a tiered layer (the ``moe_tier_state`` struct and the numpy
+    arrays it points at)."""
+
+    def __init__(self, E: int, n_slots: int):
+        import numpy as np
+
+        self.slot_of_expert = np.full(E, -1, dtype=np.int32)
+        self.expert_of_slot = np.full(n_slots, -1, dtype=np.int32)
+        self.last_use = np.zeros(n_slots, dtype=np.int64)
+        self.c = MoeTierState(E, n_slots, self.slot_of_expert.ctypes.data, self.expert_of_slot.ctypes.data,
+                              self.last_use.ctypes.data, 0)
+
+    @property
+    def tick(self) -> int:
+        return self.c.tick
+
+
+def moe_tier_plan(st: TierState, ids_host):
+    """ids_host: int32 numpy array of routed expert ids.  Returns (load_expert, load_slot)."""
+    import numpy as np
+
+    ids = np.ascontiguousarray(ids_host, dtype=np.int32).reshape(-1)
+    S = st.c.n_slots
+    le, ls = np.zeros(S, dtype=np.int32), np.zeros(S, dtype=np.int32)
+    n = ctypes.c_int32(0)
+    _check("moe_tier_plan", lib.moe_tier_plan(ctypes.byref(st.c), ids.ctypes.data, ids.size, le.ctypes.data,
+                                              ls.ctypes.data, ctypes.byref(n)))
+    return le[:n.value].copy(), ls[:n.value].copy()
+
+
+def moe_tier_load(host_w: MoeWeights, slot_w: MoeWeights, load_expert, load_slot):
+    import numpy as np
+
+    le = np.ascontiguousarray(load_expert, dtype=np.int32)
+    ls = np.ascontiguousarray(load_slot, dtype=np.int32)
+    _check("moe_tier_load", lib.moe_tier_load(ctypes.byref(host_w), ctypes.byref(slot_w), le.ctypes.data,
+                                              ls.ctypes.data, le.size, _stream()))
+
+
+def moe_tier_remap(ids: torch.Tensor, slot_of_expert: torch.Tensor, out=None):
+    _dev(ids, torch.int32, "topk_ids")
+    _dev(slot_of_expert, torch.int32, "slot_of_expert")
+    out = torch.empty_like(ids) if out is None else out
+    _check("moe_tier_remap", lib.moe_tier_remap(_ptr(ids), ids.numel(), _ptr(slot_of_expert), _ptr(out),
+                                                _stream()))
+    return out
+
+
+class TieredLayer:
+    """One low-bit layer whose E experts live in pinned host memory, with n_slots of them held on
+    the GPU as an LRU cache.  ``forward`` routes the batch, makes its experts resident, and runs
+    the layer on the slots."""
+
+    def __init__(self, fmt: int, E: int, H: int, I: int, arrays: dict, n_slots: int, device="cuda"):
+        if not 1 <= n_slots <= E:
+            raise ValueError("n_slots must be in [1, E]")
+        self.fmt, self.E, self.H, self.I, self.n_slots = fmt, E, H, I, n_slots
+        keys = ("w1_codes", "w1_scales", "w2_codes", "w2_scales")
+        self.host = {}
+        self.slot = {}
+        for key in keys:
+            a = arrays[key]
+            t = torch.from_numpy(a.view(_np_uint_as_int(a.dtype)))
+            self.host[key] = t.pin_memory()
+            self.slot[key] = torch.zeros((n_slots,) + tuple(t.shape[1:]), dtype=t.dtype, device=device)
+        self.host_c = MoeWeights(E, H, I, fmt, *(self.host[k_].data_ptr() for k_ in keys), 0, None, None, None,
+                                 None, None, 0)
+        self.slot_dw = DeviceWeights.__new__(DeviceWeights)
+        self.slot_dw.fmt, self.slot_dw.E, self.slot_dw.H, self.slot_dw.I = fmt, n_slots, H, I
+        self.slot_dw.n_hot, self.slot_dw.t = 0, self.slot
+        self.slot_dw.c = MoeWeights(n_slots, H, I, fmt, *(self.slot[k_].data_ptr() for k_ in keys), 0, None, None,
+                                    None, None, None, 0)
+        self.state = TierState(E, n_slots)
+        self.table = torch.full((E,), -1, dtype=torch.int32, device=device)
+        self.loaded = 0  # experts copied host -> device so far
+
+    def forward(self, logits: torch.Tensor, x: torch.Tensor, k: int, out_fp32: bool = True):
+        ids, gw = moe_route(logits, k)
+        ids_h = ids.cpu().numpy()  # synchronises: the plan needs this batch's experts
+        le, ls = moe_tier_plan(self.state, ids_h)
+        moe_tier_load(self.host_c, self.slot_dw.c, le, ls)
+        self.loaded += len(le)
+        self.table.copy_(torch.from_numpy(self.state.slot_of_expert), non_blocking=False)
+        sids = moe_tier_remap(ids, self.table)
+        counts, offsets, perm, inv = moe_permute(sids, self.n_slots)
+        y = moe_expert_ffn(self.slot_dw, x, k, counts, offsets, perm)
+        out = moe_combine(y, inv, gw, out_fp32=out_fp32)
+        return dict(ids=ids, slot_ids=sids, gates=gw, counts=counts, offsets=offsets, perm=perm, inv=inv,
+                    y_perm=y, out=out, n_load=len(le))

@@ -220,6 +220,56 @@ moe_status moe_quantize_w2(const float* w, int64_t rows, int32_t K, uint32_t* co
 moe_status moe_quantize_mxfp4(const float* w, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
                               void* stream);
 
+/* ---------------------------------------------------------------- host-RAM expert tier
+ * [Moet-QA] (section on what the project teaches): when the experts outgrow the GPU, most of
+ * them stay in host RAM and the GPU serves as a cache of the hot ones, which routing locality
+ * makes hit most of the work.  [Moet-README] (flagship results; launcher): the cache is an LRU
+ * over a budget of expert slots.  Reading: every expert a batch routes to is made resident
+ * before the batch runs (misses are copied host -> device, not computed elsewhere); a miss takes
+ * the lowest empty slot, else the least recently used slot that this batch does not use.
+ *
+ * Use: route the batch; copy its topk_ids to the host; moe_tier_plan; moe_tier_load the
+ * planned experts; copy slot_of_expert to the device; moe_tier_remap the ids to slot ids; run
+ * moe_permute / moe_expert_ffn / moe_combine with E = n_slots on the slot arrays (a
+ * moe_weights whose E is n_slots and whose arrays hold n_slots experts).  The per-row
+ * arithmetic is the same as with every expert resident, so the output is bit for bit the same.
+ * The tier holds low-bit experts only (no MXFP4 hot set). */
+typedef struct {
+  int32_t E;                /* experts of the layer                                          */
+  int32_t n_slots;          /* experts the GPU holds                                         */
+  int32_t* slot_of_expert;  /* host int32[E]: slot of a resident expert, -1 if not resident  */
+  int32_t* expert_of_slot;  /* host int32[n_slots]: expert in a slot, -1 if the slot is empty */
+  int64_t* last_use;        /* host int64[n_slots]: tick of the last batch that used the slot */
+  int64_t tick;             /* batches planned so far (0 for a fresh state, all slots empty) */
+} moe_tier_state;
+
+/* moe_tier_plan -- host only, no device call.  Marks the experts that ids[0..R) route to as used
+ * by the next batch (tick + 1), keeps the resident ones in place and assigns each missing one a
+ * slot, in ascending expert id order: the lowest empty slot, else the slot with the smallest
+ * last_use among the slots this batch does not use (ties: lowest slot).  Updates the state and
+ * writes the n_load experts to copy and their slots to load_expert / load_slot (host, room for
+ * n_slots entries each).
+ * Errors: INVALID_ARG (null pointer, id outside [0, E), bad sizes); UNSUPPORTED if the batch
+ * routes to more distinct experts than n_slots (the state is left unchanged: split the batch). */
+moe_status moe_tier_plan(moe_tier_state* st, const int32_t* ids, int64_t R, int32_t* load_expert,
+                         int32_t* load_slot, int32_t* n_load);
+
+/* moe_tier_load -- enqueue on `stream` the host -> device copies of the planned experts: expert
+ * load_expert[i] of host_w (E experts, arrays in host memory) into slot load_slot[i] of slot_w
+ * (n_slots experts as its E, arrays in device memory), all four arrays.  Both describe the same
+ * format (W2 or W3), H and I.  The host arrays should be pinned (hipHostMalloc) for the copies
+ * to be asynchronous; ownership stays with the caller.  load_expert / load_slot are host arrays.
+ * Errors: INVALID_ARG (format or shape mismatch, index out of range, null pointer); HIP. */
+moe_status moe_tier_load(const moe_weights* host_w, const moe_weights* slot_w, const int32_t* load_expert,
+                         const int32_t* load_slot, int32_t n_load, void* stream);
+
+/* moe_tier_remap -- slot_ids[i] = slot_of_expert[topk_ids[i]] for i < R, on the device (both
+ * tables in device memory).  Every id must be resident (moe_tier_plan makes it so); ids are not
+ * range-checked (device memory).
+ * Errors: INVALID_ARG (R < 0, null pointer with R > 0); HIP. */
+moe_status moe_tier_remap(const int32_t* topk_ids, int64_t R, const int32_t* slot_of_expert,
+                          int32_t* slot_ids, void* stream);
+
 /* moe_debug_dequant -- decode one low-bit expert matrix with the same device code the FFN
  * kernels use, into f32[rows][K] (W1: rows = 2I, K = H; W2: rows = H, K = I), in natural K
  * order.  For tests: the decoded weights must equal the format definition bit for bit.
