@@ -343,14 +343,16 @@ def measure_quantize(steps: int, warmup: int, flush_between: bool = True) -> dic
         ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
         res[name] = {"ms": ms, "weights_per_s": n / (ms * 1e-3), "GBps": n * (4 + out_b) / (ms * 1e-3) / 1e9}
     r = res["w2"]
+    workload = f"quantise W1 of 8 experts: f32[{rows}][{K}]"
     return {
         "metric": "quantiser weights/s (fp32 -> 2-bit codebook + bf16 group-32 scales)",
         "value": r["weights_per_s"], "unit": "weights/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": r["ms"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic (N(0, 0.02^2) fp32 weights, seeded torch generator)",
-        "config": {"workload": f"quantise W1 of 8 experts: f32[{rows}][{K}]", "cache_flush_between_steps": flush_between},
+        "config": {"workload": workload, "cache_flush_between_steps": flush_between},
         "roofline": {"bound": "hbm", "kernel": "quantize_w2_kernel", "achieved": r["GBps"], "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": r["GBps"] / HBM_PEAK_GBS, "traffic": None, "avg_launch_ms": r["ms"]},
+                     "unit": "GB/s", "frac": r["GBps"] / HBM_PEAK_GBS, "traffic": measured_traffic(workload),
+                     "alg_bytes_per_launch": n * (4 + 2.0 / 8 + 2.0 / 32), "avg_launch_ms": r["ms"]},
         "mxfp4": res["mxfp4"],
     }
 
@@ -448,7 +450,10 @@ def main():
               "(an expert-parallel split over several GPUs is not built)", file=sys.stderr)
         sys.exit(2)
     if args.layer == "quantize":
-        print(json.dumps(measure_quantize(args.steps, args.warmup, not args.no_flush)), flush=True)
+        res = measure_quantize(args.steps, args.warmup, not args.no_flush)
+        if args.copy_calib_mib > 0:
+            copy_calibration(args.copy_calib_mib)
+        print(json.dumps(res), flush=True)
         return
     if args.tier_slots > 0:
         import moegen

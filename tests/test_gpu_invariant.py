@@ -89,3 +89,25 @@ def test_invariant_mode_matches_oracle(L, name, override, T, sample):
     err = max_err_over_rms(host(res["out"])[toks], want)
     print(f"{name} T={T} invariant: max|err|/rms = {err:.4g}", flush=True)
     assert err <= (TOL_FP8 if sp["n_hot"] > 0 else TOL_BF16)
+
+
+def test_invariant_mode_empty_batch_and_repeated_ids(L):
+    """T = 0 is a no-op; repeated expert ids (groups larger than T) still give each row the bits
+    it gets alone."""
+    sp, dw = device_layer("tiny")
+    dw.set_batch_invariant(True)
+    x0 = torch.zeros((0, sp["H"]), dtype=torch.int16, device="cuda")
+    lg0 = torch.zeros((0, sp["E"]), dtype=torch.float32, device="cuda")
+    assert L.layer_forward(dw, lg0, x0, sp["k"])["out"].shape == (0, sp["H"])
+    k, T = 4, 40
+    b = moegen.batch(sp, T)
+    x = to_dev(b["x"])
+    ids = torch.from_numpy(np.random.default_rng(3).integers(0, 2, size=(T, k)).astype(np.int32)).cuda()
+    counts, offsets, perm, inv = L.moe_permute(ids, sp["E"])
+    y = L.moe_expert_ffn(dw, x, k, counts, offsets, perm)
+    y_tok = y[inv.long()].view(T, k, sp["H"])  # row t*k+j of token t
+    for t in (0, 17, 39):
+        ids1 = ids[t:t + 1].contiguous()
+        c1, o1, p1, i1 = L.moe_permute(ids1, sp["E"])
+        y1 = L.moe_expert_ffn(dw, x[t:t + 1].contiguous(), k, c1, o1, p1)[i1.long()]
+        assert torch.equal(y1.view(torch.int32), y_tok[t].view(torch.int32)), t

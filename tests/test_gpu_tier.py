@@ -95,3 +95,12 @@ def test_batch_over_the_slot_budget_is_refused(L):
     with pytest.raises(L.MoeError):
         tl.forward(to_dev(b["logits"]), to_dev(b["x"]), sp["k"])
     assert tl.state.tick == 0 and tl.loaded == 0
+
+
+def test_tiered_empty_batch(L):
+    sp, arrays = layer_arrays("tiny")
+    tl = L.TieredLayer(FMT[sp["fmt"]], sp["E"], sp["H"], sp["I"], arrays, 4)
+    x = torch.zeros((0, sp["H"]), dtype=torch.int16, device="cuda")
+    lg = torch.zeros((0, sp["E"]), dtype=torch.float32, device="cuda")
+    res = tl.forward(lg, x, sp["k"])
+    assert res["out"].shape == (0, sp["H"]) and res["n_load"] == 0 and tl.loaded == 0
