@@ -389,9 +389,12 @@ static int grid_for(int64_t tasks) {
 
 // K split across the waves of a workgroup, from the batch size: few tokens -> few busy
 // experts -> split K to keep every CU streaming; many tokens -> long K ranges per wave.
+// 3-bit experts (fewer, shorter rows per byte streamed) keep the two-way split up to 127 tokens,
+// where it measured faster; for 2-bit it measured slower above 16 tokens.
 // Each part keeps at least 4 steps when it can.
-static int k_split_for(int T, int K) {
-  int ks = T <= 2 ? 4 : (T <= 16 ? 2 : 1);
+static int k_split_for(int T, int K, int fmt) {
+  const int two_way_max = fmt == W3Fmt::kId ? 127 : 16;
+  int ks = T <= 2 ? 4 : (T <= two_way_max ? 2 : 1);
   while (ks > 1 && ((K / 256) % ks != 0 || (K / 256) / ks < 4)) ks /= 2;
   return ks;
 }
@@ -421,7 +424,7 @@ hipError_t launch_lowbit_fc1(const LowbitWeights& w, int E, int H, int I, int k,
                              const uint16_t* xp, const int32_t* perm, const int32_t* plan,
                              int max_items, int T, int split_T, uint16_t* hbuf, hipStream_t s) {
   (void)E;
-  const int ks = k_split_for(split_T, H);
+  const int ks = k_split_for(split_T, H, w.fmt);
   const int64_t tasks = (int64_t)max_items * ((I / 32) / (4 / ks));
   const uint32_t xb = (uint32_t)((size_t)T * H * 2);
   if (w.fmt == W2Fmt::kId)
@@ -436,7 +439,7 @@ hipError_t launch_lowbit_fc2(const LowbitWeights& w, int E, int H, int I, int k,
                              int split_T, float* y, hipStream_t s) {
   (void)E;
   (void)T;
-  const int ks = k_split_for(split_T, I);
+  const int ks = k_split_for(split_T, I, w.fmt);
   const int64_t tasks = (int64_t)max_items * ((H / 64) / (4 / ks));
   const uint32_t hb = 0;  // unused: FC2 bases its resource at each item's rows
   if (w.fmt == W2Fmt::kId)
