@@ -308,6 +308,11 @@ class TieredLayer:
     def __init__(self, fmt: int, E: int, H: int, I: int, arrays: dict, n_slots: int, device="cuda"):
         if not 1 <= n_slots <= E:
             raise ValueError("n_slots must be in [1, E]")
+        if fmt not in (MOE_FMT_W2, MOE_FMT_W3):
+            raise ValueError("the tier holds 2-bit or 3-bit experts")
+        for key in ("w1_codes", "w1_scales", "w2_codes", "w2_scales"):
+            if arrays.get(key) is None or arrays[key].shape[0] != E:
+                raise ValueError(f"{key}: expected an array with a leading axis of {E} experts")
         self.fmt, self.E, self.H, self.I, self.n_slots = fmt, E, H, I, n_slots
         keys = ("w1_codes", "w1_scales", "w2_codes", "w2_scales")
         self.host = {}
