@@ -255,10 +255,14 @@ class TierState:
     """Host-side LRU slot state of a tiered layer (the ``moe_tier_state`` struct and the numpy
     arrays it points at)."""
 
-    def __init__(self, E: int, n_slots: int):
+    def __init__(self, E: int, n_slots: int, slot_of_expert=None):
         import numpy as np
 
-        self.slot_of_expert = np.full(E, -1, dtype=np.int32)
+        if slot_of_expert is None:
+            slot_of_expert = np.full(E, -1, dtype=np.int32)
+        assert slot_of_expert.dtype == np.int32 and slot_of_expert.shape == (E,) and slot_of_expert.flags.c_contiguous
+        slot_of_expert[:] = -1
+        self.slot_of_expert = slot_of_expert
         self.expert_of_slot = np.full(n_slots, -1, dtype=np.int32)
         self.last_use = np.zeros(n_slots, dtype=np.int64)
         self.c = MoeTierState(E, n_slots, self.slot_of_expert.ctypes.data, self.expert_of_slot.ctypes.data,
@@ -329,17 +333,26 @@ class TieredLayer:
         self.slot_dw.n_hot, self.slot_dw.t = 0, self.slot
         self.slot_dw.c = MoeWeights(n_slots, H, I, fmt, *(self.slot[k_].data_ptr() for k_ in keys), 0, None, None,
                                     None, None, None, 0)
-        self.state = TierState(E, n_slots)
+        # the slot table lives in pinned host memory (the plan writes it in place) and is copied
+        # to the device asynchronously; the next plan runs only after the next batch's ids have
+        # been read back, i.e. after that copy has completed
+        self.table_h = torch.full((E,), -1, dtype=torch.int32).pin_memory()
+        self.state = TierState(E, n_slots, self.table_h.numpy())
         self.table = torch.full((E,), -1, dtype=torch.int32, device=device)
+        self.ids_h = torch.empty(0, dtype=torch.int32).pin_memory()
         self.loaded = 0  # experts copied host -> device so far
 
     def forward(self, logits: torch.Tensor, x: torch.Tensor, k: int, out_fp32: bool = True):
         ids, gw = moe_route(logits, k)
-        ids_h = ids.cpu().numpy()  # synchronises: the plan needs this batch's experts
-        le, ls = moe_tier_plan(self.state, ids_h)
+        R = ids.numel()
+        if self.ids_h.numel() < R:
+            self.ids_h = torch.empty(R, dtype=torch.int32).pin_memory()
+        self.ids_h[:R].copy_(ids.view(-1), non_blocking=True)
+        torch.cuda.current_stream().synchronize()  # the plan needs this batch's experts
+        le, ls = moe_tier_plan(self.state, self.ids_h[:R].numpy())
         moe_tier_load(self.host_c, self.slot_dw.c, le, ls)
         self.loaded += len(le)
-        self.table.copy_(torch.from_numpy(self.state.slot_of_expert), non_blocking=False)
+        self.table.copy_(self.table_h, non_blocking=True)
         sids = moe_tier_remap(ids, self.table)
         counts, offsets, perm, inv = moe_permute(sids, self.n_slots)
         y = moe_expert_ffn(self.slot_dw, x, k, counts, offsets, perm)
