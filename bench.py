@@ -169,17 +169,25 @@ def measure(sp: dict, dw, T: int, steps: int, warmup: int, flush_between: bool =
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
+    # with a hot set, the hot experts' preparation and MXFP4 -> FP8 conversion run on a second
+    # stream, concurrent with the low-bit stages
+    side = torch.cuda.Stream() if sp["n_hot"] > 0 else None
+
     def step(evs=None):
         if evs:
             evs[0].record(stream)
         L.moe_route(logits, k, ids, gw)
         L.moe_permute(ids, E, ws=ws_p, out=(counts, offsets, perm, inv))
-        for s in range(n_stages):
-            if evs:
-                evs[1 + 2 * s].record(stream)
-            L.moe_expert_ffn_stage(dw, x, k, counts, offsets, perm, y, ws_f, s)
-            if evs:
-                evs[2 + 2 * s].record(stream)
+        stage_evs = {s: (evs[1 + 2 * s], evs[2 + 2 * s]) for s in range(n_stages)} if evs else None
+        if side is not None:
+            L.moe_expert_ffn_two_streams(dw, x, k, counts, offsets, perm, y, ws_f, side, stage_evs)
+        else:
+            for s in range(n_stages):
+                if evs:
+                    evs[1 + 2 * s].record(stream)
+                L.moe_expert_ffn_stage(dw, x, k, counts, offsets, perm, y, ws_f, s)
+                if evs:
+                    evs[2 + 2 * s].record(stream)
         L.moe_combine(y, inv, gw, out_fp32=False, out=out)
         if evs:
             evs[-1].record(stream)
@@ -306,7 +314,8 @@ def measure(sp: dict, dw, T: int, steps: int, warmup: int, flush_between: bool =
         "roofline": roof,
         "step_timing": "HIP graph replay" if graph_ms else "eager launches",
         "ms_per_step_eager": eager_ms,
-        "stages_ms": {"route+permute+prepare+combine (eager)": eager_ms - fc1_ms - fc2_ms - conv_ms - hot_fc1_ms - hot_fc2_ms,
+        "hot_convert_overlapped": side is not None,
+        "stages_ms": {"route+permute+prepare+combine (eager; stage sum for one stream)": eager_ms - fc1_ms - fc2_ms - conv_ms - hot_fc1_ms - hot_fc2_ms,
                       "fc1": fc1_ms, "fc2": fc2_ms, "hot_convert": conv_ms, "hot_fc1": hot_fc1_ms, "hot_fc2": hot_fc2_ms},
         "ffn_stage_ms": [float(np.mean(v)) for v in stage_ms],
         "weight_GBps_fc1_fc2": (w1b + w2b) / ((fc1_ms + fc2_ms + hot_fc1_ms + hot_fc2_ms) * 1e-3) / 1e9,

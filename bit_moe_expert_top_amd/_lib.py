@@ -186,6 +186,50 @@ def moe_expert_ffn_stage(w: DeviceWeights, x: torch.Tensor, k: int, counts, offs
                                                             ws.numel(), stage, _stream()))
 
 
+LOWBIT_STAGES = 5  # stages 0..4: prepare, FC1 (stream, GEMM), FC2 (stream, GEMM); 5: hot prepare
+
+
+def moe_expert_ffn_two_streams(w: DeviceWeights, x: torch.Tensor, k: int, counts, offsets, perm, y_perm, ws,
+                               side: torch.cuda.Stream, stage_events=None):
+    """moe_expert_ffn with the hot experts' preparation and first MXFP4 -> FP8 conversion on a
+    second stream, concurrent with the low-bit stages (they touch disjoint workspace regions
+    and rows); the FP8 matmuls start once both are done.  Same kernels and inputs as the
+    one-stream call, so the same output bits.  stage_events: optional {stage: (start, end)} HIP
+    events recorded around each stage on the stream that runs it."""
+    T = x.shape[0]
+    n = moe_expert_ffn_num_stages(w, T, k, ws.numel())
+    main = torch.cuda.current_stream()
+
+    def run(st):
+        ev = stage_events.get(st) if stage_events else None
+        if ev:
+            ev[0].record(torch.cuda.current_stream())
+        moe_expert_ffn_stage(w, x, k, counts, offsets, perm, y_perm, ws, st)
+        if ev:
+            ev[1].record(torch.cuda.current_stream())
+
+    if n <= LOWBIT_STAGES + 1:  # no hot set (or nothing to convert): one stream
+        for st in range(n):
+            run(st)
+        return y_perm
+    fork = torch.cuda.Event()
+    fork.record(main)
+    side.wait_event(fork)
+    with torch.cuda.stream(side):
+        run(LOWBIT_STAGES)        # hot work list, MXFP8 of x
+        run(LOWBIT_STAGES + 1)    # first batch of hot experts: MXFP4 -> FP8 into the slots
+        join = torch.cuda.Event()
+        join.record(side)
+    for st in range(LOWBIT_STAGES):
+        run(st)
+    main.wait_event(join)
+    for st in range(LOWBIT_STAGES + 2, n):
+        run(st)
+    for t in (x, counts, offsets, perm, y_perm, ws):
+        t.record_stream(side)
+    return y_perm
+
+
 def moe_combine(y_perm: torch.Tensor, inv: torch.Tensor, topk_w: torch.Tensor, out_fp32: bool = False,
                 out=None):
     T, k = topk_w.shape
