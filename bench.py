@@ -119,7 +119,15 @@ def cpu_baseline(sp, batch, T, n_tok):
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
-    return {"value": passes * n_tok / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    try:  # the threads numpy's BLAS used for the matmuls
+        from threadpoolctl import threadpool_info
+
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        blas_threads = max((i.get("num_threads") or 0) for i in blas) if blas else None
+    except ImportError:
+        blas_threads = None
+    return {"value": passes * n_tok / dt, "unit": "tokens/s", "cores": cores, "blas_threads": blas_threads,
+            "kind": "oracle",
             "sample": f"first {n_tok} of the {T} tokens ({len(used)} experts), numpy fp64, {passes} passes "
                       f"in {dt:.1f} s"}
 
