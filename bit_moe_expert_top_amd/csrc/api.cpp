@@ -28,14 +28,13 @@ constexpr int kStreamChunk = 32;
 // grouped-GEMM kernels (items of kGemmRows rows); smaller groups always stream.
 constexpr int kGemmMinTokens = 128;
 
-// Batch-invariant mode: every group streams, in items of 16 rows, and the streaming kernels
-// take the K split of a one-token batch (it then depends on H and I only).  A row's sums are
-// formed in the same order whatever T is: the kernels treat each token column on its own.
+// Batch-invariant mode: every group streams, and the streaming kernels take the K split of a
+// 16-token batch whatever T is (it then depends on H, I and the format only).  A row's sums are
+// formed in the same order for every T: the split fixes how K is cut and summed, and the kernels
+// treat each token column of a tile on its own, so the item size (16 or 32 rows) does not matter.
 inline bool invariant(const moe_weights* w) { return (w->flags & MOE_FLAG_BATCH_INVARIANT) != 0; }
-inline int stream_chunk(const moe_weights* w, int T) {
-  return (T <= 16 || invariant(w)) ? 16 : kStreamChunk;
-}
-inline int split_tokens(const moe_weights* w, int T) { return invariant(w) ? 1 : T; }
+inline int stream_chunk(int T) { return T <= 16 ? 16 : kStreamChunk; }
+inline int split_tokens(const moe_weights* w, int T) { return invariant(w) ? 16 : T; }
 
 // Hot experts are computed by the FP8 grouped GEMM on items of this many rows.
 constexpr int kHotChunk = 128;
@@ -56,7 +55,7 @@ FfnLayout ffn_layout(const moe_weights* w, int T, int k) {
   const int64_t R = (int64_t)T * k;
   L.gemm = T >= kGemmMinTokens && !invariant(w);
   const int64_t per_expert = R < w->E ? R : w->E;  // one partial item per expert at most
-  const int chunk = stream_chunk(w, T);
+  const int chunk = stream_chunk(T);
   L.max_items_s = (R + chunk - 1) / chunk + per_expert;
   L.max_items_g = L.gemm ? (R + kGemmRows - 1) / kGemmRows + per_expert : 0;
   size_t off = 0;
@@ -235,7 +234,7 @@ moe_status ffn_run_stage(const moe_weights* w, const uint16_t* x, int32_t T, int
   hipError_t e = hipSuccess;
   switch (stage) {
     case 0:
-      e = launch_prepare(offsets, w->E, stream_chunk(w, T), kGemmRows, L.gemm, w->hot_ids, w->n_hot, plan_s, plan_g,
+      e = launch_prepare(offsets, w->E, stream_chunk(T), kGemmRows, L.gemm, w->hot_ids, w->n_hot, plan_s, plan_g,
                          x, T, w->H, lw.fmt, xp, s);
       break;
     case 1:

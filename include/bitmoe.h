@@ -97,7 +97,7 @@ typedef struct {
  * the same logits at any batch size.
  * With this flag moe_expert_ffn computes every grouped row with one accumulation order that
  * does not depend on T or on the other rows of the batch (the streaming kernels for every group,
- * with one K split chosen from H and I alone), so a token's output has the same bits whatever
+ * with one K split chosen from H, I and the format alone), so a token's output has the same bits whatever
  * batch it comes in.  Without it the K split follows T and large groups of large batches run on
  * the grouped-GEMM kernels: faster, and the bits of a token may change with T (the values
  * stay within the same tolerance of the exact result).  Routing, grouping, the FP8 hot path
