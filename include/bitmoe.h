@@ -49,7 +49,7 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = -1, /* null pointer, bad size or shape, k out of range        */
-  MOE_ERR_UNSUPPORTED = -2, /* a valid request this build does not implement            */
+  MOE_ERR_UNSUPPORTED = -2, /* a valid request the library does not implement           */
   MOE_ERR_WORKSPACE = -3,   /* ws_bytes smaller than the matching *_ws_bytes() query    */
   MOE_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed                */
 } moe_status;
