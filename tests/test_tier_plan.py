@@ -119,3 +119,17 @@ def test_load_and_remap_argument_checks(L):
     assert L.lib.moe_tier_load(ctypes.byref(host), ctypes.byref(slots), e, s, 0, None) == 0   # nothing to do
     assert L.lib.moe_tier_remap(None, 4, p, p, None) == -1
     assert L.lib.moe_tier_remap(None, 0, None, None, None) == 0
+
+
+def test_tiered_layer_argument_checks(L):
+    """Checked before any device memory is touched (runs without a GPU)."""
+    arrays = {key: np.zeros((8, 4), dtype=np.uint32) for key in ("w1_codes", "w1_scales", "w2_codes", "w2_scales")}
+    with pytest.raises(ValueError):
+        L.TieredLayer(L.MOE_FMT_W2, 8, 256, 512, arrays, 0)           # no slots
+    with pytest.raises(ValueError):
+        L.TieredLayer(L.MOE_FMT_W2, 8, 256, 512, arrays, 9)           # more slots than experts
+    with pytest.raises(ValueError):
+        L.TieredLayer(L.MOE_FMT_MXFP4, 8, 256, 512, arrays, 4)        # the tier holds 2-/3-bit experts
+    bad = dict(arrays, w2_scales=np.zeros((7, 4), dtype=np.uint32))
+    with pytest.raises(ValueError):
+        L.TieredLayer(L.MOE_FMT_W2, 8, 256, 512, bad, 4)              # expert axis of the wrong length
