@@ -111,3 +111,21 @@ def test_invariant_mode_empty_batch_and_repeated_ids(L):
         c1, o1, p1, i1 = L.moe_permute(ids1, sp["E"])
         y1 = L.moe_expert_ffn(dw, x[t:t + 1].contiguous(), k, c1, o1, p1)[i1.long()]
         assert torch.equal(y1.view(torch.int32), y_tok[t].view(torch.int32)), t
+
+
+def test_invariant_mode_with_fewer_slots_than_hot_experts(L):
+    """Hot experts converted and computed in batches of 5 slots: a token's bits do not depend on
+    the batch it comes in, nor on the slot count."""
+    sp, dw = device_layer("mixed")
+    dw.set_batch_invariant(True)
+    k = sp["k"]
+    b = moegen.batch(sp, 300)
+    x, lg = to_dev(b["x"]), to_dev(b["logits"])
+    full = L.layer_forward(dw, lg, x, k, fp8_slots=5)["out"].view(torch.int32)
+    full_all = L.layer_forward(dw, lg, x, k)["out"].view(torch.int32)
+    assert torch.equal(full, full_all)
+    for idx in (np.array([17]), np.arange(0, 300, 7)):
+        ti = torch.from_numpy(idx).cuda()
+        print(f"mixed, 5 slots: T={len(idx)}", flush=True)
+        sub = L.layer_forward(dw, lg[ti].contiguous(), x[ti].contiguous(), k, fp8_slots=5)["out"]
+        assert torch.equal(sub.view(torch.int32), full[ti])
