@@ -396,7 +396,8 @@ def copy_calibration(mib: int):
     print(f"[bench] copy calibration: {mib} MiB read + {mib} MiB written", file=sys.stderr, flush=True)
 
 
-def measure_tier(sp: dict, arrays: dict, T: int, n_slots: int, steps: int, warmup: int) -> dict:
+def measure_tier(sp: dict, arrays: dict, T: int, n_slots: int, steps: int, warmup: int,
+                 pipelined: bool = False) -> dict:
     """The layer with its experts in pinned host memory and n_slots of them on the GPU (an LRU
     cache): every step is a new batch of T tokens, so misses are copied host -> device inside the
     timed step (which also synchronises once, for the plan).  Wall-clock time per step."""
@@ -413,8 +414,11 @@ def measure_tier(sp: dict, arrays: dict, T: int, n_slots: int, steps: int, warmu
     x = torch.from_numpy(pool["x"].view(np.int16)).cuda()
     per_expert = weight_bytes_per_expert(sp, 1) + weight_bytes_per_expert(sp, 2)
     stream = torch.cuda.current_stream()
-    for i in range(warmup):
-        tl.forward(lg[i * T:(i + 1) * T], x[i * T:(i + 1) * T], k)
+    if pipelined:
+        tl.forward_pipelined([(lg[i * T:(i + 1) * T], x[i * T:(i + 1) * T]) for i in range(warmup)], k)
+    else:
+        for i in range(warmup):
+            tl.forward(lg[i * T:(i + 1) * T], x[i * T:(i + 1) * T], k)
     torch.cuda.synchronize()
     loaded0 = tl.loaded
     ms, load_ms, routed = [], [], 0
@@ -427,9 +431,19 @@ def measure_tier(sp: dict, arrays: dict, T: int, n_slots: int, steps: int, warmu
         e1.record(stream)
         load_ms.append((e0, e1))
 
+    if pipelined:
+        # the copies of step i+1 overlap the FFN of step i (second stream); one timed sequence
+        batches = [(lg[i * T:(i + 1) * T], x[i * T:(i + 1) * T]) for i in range(warmup, warmup + steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        outs = tl.forward_pipelined(batches, k)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3
+        ms = [wall_ms / steps] * steps
+        routed = sum(int((torch.bincount(o["ids"].view(-1).long(), minlength=sp["E"]) > 0).sum().item()) for o in outs)
     L.moe_tier_load = timed_load
     try:
-        for i in range(warmup, warmup + steps):
+        for i in (range(0) if pipelined else range(warmup, warmup + steps)):
             t0 = time.perf_counter()
             r = tl.forward(lg[i * T:(i + 1) * T], x[i * T:(i + 1) * T], k)
             torch.cuda.synchronize()
@@ -438,17 +452,18 @@ def measure_tier(sp: dict, arrays: dict, T: int, n_slots: int, steps: int, warmu
     finally:
         L.moe_tier_load = orig_load
     loads = tl.loaded - loaded0
-    copy_ms = float(sum(a.elapsed_time(b) for a, b in load_ms))
+    copy_ms = float(sum(a.elapsed_time(b) for a, b in load_ms)) if not pipelined else 0.0
     step_ms = float(np.mean(ms))
     return {
         "metric": METRIC, "value": T / (step_ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
         "warmup": warmup, "ms_per_step": step_ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded), a new batch every step",
         "config": {"workload": f"{sp['name']} MoE layer E={sp['E']} top-{k} H={sp['H']} I={sp['I']} {sp['fmt']} "
-                               f"T={T}, experts in pinned host RAM, {n_slots} GPU slots (LRU)", "tokens": T},
+                               f"T={T}, experts in pinned host RAM, {n_slots} GPU slots (LRU)"
+                               + (", copies of step i+1 overlapped with step i" if pipelined else ""), "tokens": T},
         "tier": {"slots": n_slots, "experts_used_per_step": routed / steps, "loads_per_step": loads / steps,
                  "hit_rate": 1.0 - loads / max(1, routed), "h2d_bytes_per_step": loads * per_expert / steps,
-                 "h2d_ms_per_step": copy_ms / steps,
+                 "h2d_ms_per_step": copy_ms / steps if not pipelined else None,
                  "h2d_GBps": loads * per_expert / (copy_ms * 1e-3) / 1e9 if copy_ms > 0 else None},
     }
 
@@ -463,6 +478,8 @@ def main():
     ap.add_argument("--no-flush", action="store_true", help="do not flush caches between steps")
     ap.add_argument("--tier-slots", type=int, default=0,
                     help="keep the experts in pinned host RAM with this many GPU slots (LRU); 0 = all resident")
+    ap.add_argument("--tier-pipeline", action="store_true",
+                    help="with --tier-slots: overlap the copies of step i+1 with the FFN of step i")
     ap.add_argument("--batch-invariant", action="store_true",
                     help="run the layer in its batch-invariant mode (same bits for a token at any T)")
     ap.add_argument("--cpu-tokens", type=int, default=64, help="tokens of the oracle's timed sample (0 = skip)")
@@ -483,8 +500,8 @@ def main():
         import moegen
 
         sp = moegen.spec(args.layer)
-        print(json.dumps(measure_tier(sp, moegen.weights(sp), args.T, args.tier_slots, args.steps, args.warmup)),
-              flush=True)
+        print(json.dumps(measure_tier(sp, moegen.weights(sp), args.T, args.tier_slots, args.steps, args.warmup,
+                                      args.tier_pipeline)), flush=True)
         return
     sp, dw = setup_layer(args.layer)
     dw.set_batch_invariant(args.batch_invariant)

@@ -385,6 +385,8 @@ class TieredLayer:
         self.table = torch.full((E,), -1, dtype=torch.int32, device=device)
         self.ids_h = torch.empty(0, dtype=torch.int32).pin_memory()
         self.loaded = 0  # experts copied host -> device so far
+        self._table2 = None
+        self._side = None
 
     def forward(self, logits: torch.Tensor, x: torch.Tensor, k: int, out_fp32: bool = True):
         ids, gw = moe_route(logits, k)
@@ -403,3 +405,61 @@ class TieredLayer:
         out = moe_combine(y, inv, gw, out_fp32=out_fp32)
         return dict(ids=ids, slot_ids=sids, gates=gw, counts=counts, offsets=offsets, perm=perm, inv=inv,
                     y_perm=y, out=out, n_load=len(le))
+
+    def forward_pipelined(self, batches, k: int, out_fp32: bool = True):
+        """A sequence of independent batches [(logits, x), ...] with the copies of batch i+1
+        overlapping the FFN of batch i: batch i+1 is routed, planned and loaded on a second
+        stream while the main stream computes batch i.  Its plan counts batch i's experts as
+        used too, so none of the slots batch i reads is evicted (the slot budget must hold the
+        experts of two consecutive batches); its loads wait until batch i-1 is done.  Returns
+        the outputs in order; each is bit-equal to `forward` on that batch alone."""
+        import numpy as np
+
+        if self._side is None:
+            self._side = torch.cuda.Stream()
+            self._table2 = torch.full_like(self.table, -1)
+        main, side = torch.cuda.current_stream(), self._side
+        tables = (self.table, self._table2)
+
+        def stage_in(i, prev_ids, wait_done):
+            lg = batches[i][0]
+            with torch.cuda.stream(side):
+                ids, gw = moe_route(lg, k)
+                ids_h = torch.empty(ids.numel(), dtype=torch.int32).pin_memory()
+                ids_h.copy_(ids.view(-1), non_blocking=True)
+                got = torch.cuda.Event()
+                got.record(side)
+            got.synchronize()
+            ids_np = ids_h.numpy()
+            need = ids_np if prev_ids is None else np.concatenate([ids_np, prev_ids])
+            le, ls = moe_tier_plan(self.state, need)
+            with torch.cuda.stream(side):
+                if wait_done is not None:
+                    side.wait_event(wait_done)  # batch i-2 has left its slots and its slot table
+                moe_tier_load(self.host_c, self.slot_dw.c, le, ls)
+                tables[i % 2].copy_(self.table_h, non_blocking=True)
+                ready = torch.cuda.Event()
+                ready.record(side)
+            self.loaded += len(le)
+            return ids, gw, ids_np, ready, len(le)
+
+        side.wait_stream(main)  # the inputs were written on the main stream before this call
+        outs, done = [], []
+        nxt = stage_in(0, None, None) if batches else None
+        for i in range(len(batches)):
+            ids, gw, ids_np, ready, nl = nxt
+            main.wait_event(ready)
+            ids.record_stream(main)
+            gw.record_stream(main)
+            x = batches[i][1]
+            sids = moe_tier_remap(ids, tables[i % 2])
+            counts, offsets, perm, inv = moe_permute(sids, self.n_slots)
+            y = moe_expert_ffn(self.slot_dw, x, k, counts, offsets, perm)
+            out = moe_combine(y, inv, gw, out_fp32=out_fp32)
+            ev = torch.cuda.Event()
+            ev.record(main)
+            done.append(ev)
+            outs.append(dict(ids=ids, out=out, n_load=nl))
+            if i + 1 < len(batches):
+                nxt = stage_in(i + 1, ids_np, done[i - 1] if i >= 1 else None)
+        return outs

@@ -104,3 +104,27 @@ def test_tiered_empty_batch(L):
     lg = torch.zeros((0, sp["E"]), dtype=torch.float32, device="cuda")
     res = tl.forward(lg, x, sp["k"])
     assert res["out"].shape == (0, sp["H"]) and res["n_load"] == 0 and tl.loaded == 0
+
+
+@pytest.mark.parametrize("name,override,slots,T", [("decode", {}, 24, 1), ("decode", {}, 96, 4),
+                                                   ("w3", {"E": 32}, 24, 1), ("tiny", {}, 8, 2)])
+def test_pipelined_tier_matches_resident(L, name, override, slots, T):
+    """Batch i+1 routed, planned and loaded on a second stream while batch i computes: every
+    output bit-equal to the all-resident layer; batch i's slots survive batch i+1's plan."""
+    sp, arrays = layer_arrays(name, **override)
+    _, dw = device_layer(name, **override)
+    tl = L.TieredLayer(FMT[sp["fmt"]], sp["E"], sp["H"], sp["I"], arrays, slots)
+    k, nb = sp["k"], 12
+    pool = moegen.batch(sp, nb * T)
+    lg_all, x_all = to_dev(pool["logits"]), to_dev(pool["x"])
+    batches = [(lg_all[b * T:(b + 1) * T].contiguous(), x_all[b * T:(b + 1) * T].contiguous()) for b in range(nb)]
+    print(f"{name} slots={slots} T={T}: {nb} pipelined batches", flush=True)
+    outs = tl.forward_pipelined(batches, k)
+    torch.cuda.synchronize()
+    for b, (lg, x) in enumerate(batches):
+        want = L.layer_forward(dw, lg, x, k)
+        assert torch.equal(outs[b]["ids"], want["ids"])
+        assert torch.equal(outs[b]["out"].view(torch.int32), want["out"].view(torch.int32)), f"batch {b}"
+    loads = [o["n_load"] for o in outs]
+    print(f"{name}: experts loaded per batch {loads}", flush=True)
+    assert tl.loaded == sum(loads) and loads[0] > 0
