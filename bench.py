@@ -304,6 +304,17 @@ def measure(sp: dict, dw, T: int, steps: int, warmup: int, flush_between: bool =
     roof["traffic"] = measured_traffic(workload)
     roof["avg_launch_ms"] = roof_ms
     all_flops = 2.0 * R * 3 * I * H
+    # the whole layer against its roofline: t_roof = max(flops_bf16 / P_bf16 + flops_fp8 / P_fp8,
+    # algorithmic bytes / HBM peak), with the bytes = packed weights of the experts that received
+    # rows + logits + x + out (bf16)
+    f_fp8 = 2.0 * hot_rows * 3 * I * H
+    f_bf16 = all_flops - f_fp8
+    t_mfma = (f_bf16 / (BF16_PEAK_TFLOPS * 1e12) + f_fp8 / (FP8_PEAK_TFLOPS * 1e12)) * 1e3
+    layer_bytes = w1b + w2b + T * E * 4 + T * H * 2 + T * H * 2
+    t_hbm = layer_bytes / (HBM_PEAK_GBS * 1e9) * 1e3
+    layer_roof = {"bound": "mfma" if t_mfma > t_hbm else "hbm", "t_roof_ms": max(t_mfma, t_hbm),
+                  "t_mfma_ms": t_mfma, "t_hbm_ms": t_hbm, "flops": all_flops, "alg_bytes": layer_bytes,
+                  "frac": max(t_mfma, t_hbm) / ms}
     return {
         "metric": METRIC,
         "value": T / (ms * 1e-3),
@@ -320,6 +331,7 @@ def measure(sp: dict, dw, T: int, steps: int, warmup: int, flush_between: bool =
         "config": {"workload": workload, "tokens": T, "experts_active": n_active,
                    "cache_flush_between_steps": flush_between, "batch_invariant": batch_invariant},
         "roofline": roof,
+        "layer_roofline": layer_roof,
         "step_timing": "HIP graph replay" if graph_ms else "eager launches",
         "ms_per_step_eager": eager_ms,
         "hot_convert_overlapped": side is not None,
@@ -332,6 +344,25 @@ def measure(sp: dict, dw, T: int, steps: int, warmup: int, flush_between: bool =
         "ms_per_step_median": float(np.median(graph_ms or step_ms)),
         "wall_s_timed_loop_incl_flush": wall,
     }
+
+
+def extra_measurement(name: str, T: int, steps: int, warmup: int) -> dict:
+    """A second workload in the same run (its own layer, freed afterwards): the prefill half of
+    the metric (grouped-GEMM MFMA fraction) and the mixed layer (FP8 MFMA fraction)."""
+    import gc
+
+    import torch
+
+    sp, dw = setup_layer(name)
+    r = measure(sp, dw, T, steps, warmup)
+    del dw
+    gc.collect()
+    torch.cuda.empty_cache()
+    return {"workload": r["config"]["workload"], "value": r["value"], "unit": r["unit"],
+            "ms_per_step": r["ms_per_step"], "steps": steps, "warmup": warmup,
+            "experts_active": r["config"]["experts_active"], "roofline": r["roofline"],
+            "layer_roofline": r["layer_roofline"], "stages_ms": r["stages_ms"],
+            "step_timing": r["step_timing"]}
 
 
 def measure_quantize(steps: int, warmup: int, flush_between: bool = True) -> dict:
@@ -483,6 +514,9 @@ def main():
     ap.add_argument("--batch-invariant", action="store_true",
                     help="run the layer in its batch-invariant mode (same bits for a token at any T)")
     ap.add_argument("--cpu-tokens", type=int, default=64, help="tokens of the oracle's timed sample (0 = skip)")
+    ap.add_argument("--extras", default="prefill,mixed",
+                    help="with the default decode T=64 run, also measure these workloads in the same run "
+                         "(prefill = T 8192, mixed = T 4096; empty = none)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after timing, run a plain copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -508,6 +542,19 @@ def main():
     res = measure(sp, dw, args.T, args.steps, args.warmup, not args.no_flush, args.batch_invariant)
     if args.copy_calib_mib > 0:
         copy_calibration(args.copy_calib_mib)
+    extras = [e for e in args.extras.split(",") if e] if (args.layer == "decode" and args.T == 64
+                                                          and not args.batch_invariant) else []
+    if extras:
+        import gc
+
+        import torch
+
+        del dw
+        gc.collect()
+        torch.cuda.empty_cache()
+        sizes = {"prefill": 8192, "mixed": 4096}
+        for name in extras:
+            res[name] = extra_measurement(name, sizes[name], min(args.steps, 10), min(args.warmup, 3))
     if args.cpu_tokens > 0:
         import moegen
 

@@ -59,6 +59,9 @@ _SIGS = {
     "moe_quantize_w2": (_i32, [_p, _i64, _i32, _p, _p, _p]),
     "moe_quantize_mxfp4": (_i32, [_p, _i64, _i32, _p, _p, _p]),
     "moe_debug_dequant": (_i32, [ctypes.POINTER(MoeWeights), _i32, _i32, _p, _p]),
+    "moe_expert_ffn_ws_region": (_i32, [ctypes.POINTER(MoeWeights), _i32, _i32, _sz, _i32,
+                                        ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
+    "moe_fp8_slot_layout": (_i32, [_i32, _i32] + [ctypes.POINTER(_sz)] * 5),
     "moe_status_str": (ctypes.c_char_p, [_i32]),
     "moe_tier_plan": (_i32, [ctypes.POINTER(MoeTierState), _p, _i64, _p, _p, _p]),
     "moe_tier_load": (_i32, [ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeWeights), _p, _p, _i32, _p]),
@@ -277,8 +280,28 @@ def moe_quantize_mxfp4(w: torch.Tensor):
     return codes, sc
 
 
+MOE_WS_XQ, MOE_WS_XQ_SCALES, MOE_WS_HQ, MOE_WS_HQ_SCALES, MOE_WS_SLOTS = 1, 2, 3, 4, 5
+
+
+def moe_expert_ffn_ws_region(w: DeviceWeights, T: int, k: int, ws_bytes: int, region: int):
+    """(byte offset, bytes) of an intermediate of moe_expert_ffn inside its workspace."""
+    off, n = _sz(0), _sz(0)
+    _check("moe_expert_ffn_ws_region", lib.moe_expert_ffn_ws_region(ctypes.byref(w.c), T, k, ws_bytes, region,
+                                                                    ctypes.byref(off), ctypes.byref(n)))
+    return off.value, n.value
+
+
+def moe_fp8_slot_layout(H: int, I: int) -> dict:
+    """Byte offsets of W1, W1 scales, W2, W2 scales inside one FP8 slot, and the slot size."""
+    v = [_sz(0) for _ in range(5)]
+    _check("moe_fp8_slot_layout", lib.moe_fp8_slot_layout(H, I, *(ctypes.byref(x) for x in v)))
+    return dict(zip(("w1", "w1_scales", "w2", "w2_scales", "slot_bytes"), (x.value for x in v)))
+
+
 def moe_debug_dequant(w: DeviceWeights, e: int, which: int):
-    rows, K = (2 * w.I, w.H) if which == 1 else (w.H, w.I)
+    """which: 1 / 2 = W1 / W2 through the streaming kernels' decoder, 3 / 4 through the grouped
+    GEMM's decoder."""
+    rows, K = (2 * w.I, w.H) if which in (1, 3) else (w.H, w.I)
     out = torch.empty((rows, K), dtype=torch.float32, device="cuda")
     _check("moe_debug_dequant", lib.moe_debug_dequant(ctypes.byref(w.c), e, which, _ptr(out), _stream()))
     return out

@@ -99,8 +99,12 @@ int ffn_slots(const moe_weights* w, const FfnLayout& L, size_t ws_bytes) {
 moe_status check_weights(const moe_weights* w) {
   if (!w) return MOE_ERR_INVALID_ARG;
   if (w->E < 1 || w->E > kMaxE || w->H <= 0 || w->I <= 0) return MOE_ERR_INVALID_ARG;
-  if (w->H % 256 || w->I % 256 || w->H > 16384 || w->I > 16384) return MOE_ERR_INVALID_ARG;
   if (w->fmt != MOE_FMT_W2 && w->fmt != MOE_FMT_W3) return MOE_ERR_INVALID_ARG;
+  // a shape the formats define: whole scale groups along K (32 weights, 64 for 3-bit)
+  const int group = w->fmt == MOE_FMT_W3 ? 64 : 32;
+  if (w->H % group || w->I % group) return MOE_ERR_INVALID_ARG;
+  // shapes the kernels are built for: whole 256-k steps, at most 16384
+  if (w->H % 256 || w->I % 256 || w->H > 16384 || w->I > 16384) return MOE_ERR_UNSUPPORTED;
   if (!w->w1_codes || !w->w1_scales || !w->w2_codes || !w->w2_scales) return MOE_ERR_INVALID_ARG;
   if (w->n_hot < 0 || w->n_hot > w->E) return MOE_ERR_INVALID_ARG;
   if (w->flags & ~MOE_FLAG_BATCH_INVARIANT) return MOE_ERR_INVALID_ARG;
@@ -112,6 +116,7 @@ moe_status check_weights(const moe_weights* w) {
 
 HotWeights hot(const moe_weights* w) {
   HotWeights h;
+  h.E = w->E;
   h.n_hot = w->n_hot;
   h.hot_ids = w->hot_ids;
   h.w1_codes = static_cast<const uint8_t*>(w->hot_w1_codes);
@@ -353,9 +358,45 @@ moe_status moe_debug_dequant(const moe_weights* w, int32_t e, int32_t which, flo
                              void* stream) {
   moe_status st = check_weights(w);
   if (st != MOE_OK) return st;
-  if (e < 0 || e >= w->E || (which != 1 && which != 2) || !out) return MOE_ERR_INVALID_ARG;
-  return from_hip(launch_debug_dequant(lowbit(w), w->E, w->H, w->I, e, which, out,
-                                       as_stream(stream)));
+  if (e < 0 || e >= w->E || which < 1 || which > 4 || !out) return MOE_ERR_INVALID_ARG;
+  if (which <= 2)
+    return from_hip(launch_debug_dequant(lowbit(w), w->E, w->H, w->I, e, which, out, as_stream(stream)));
+  return from_hip(launch_debug_dequant_gemm(lowbit(w), w->H, w->I, e, which - 2, out, as_stream(stream)));
+}
+
+moe_status moe_expert_ffn_ws_region(const moe_weights* w, int32_t T, int32_t k, size_t ws_bytes,
+                                    int32_t region, size_t* offset, size_t* bytes) {
+  moe_status st = check_weights(w);
+  if (st != MOE_OK) return st;
+  if (T < 1 || k < 1 || k > w->E || (int64_t)T * k >= ((int64_t)1 << 31) || !offset || !bytes)
+    return MOE_ERR_INVALID_ARG;
+  if (region < MOE_WS_XQ || region > MOE_WS_SLOTS) return MOE_ERR_INVALID_ARG;
+  if (w->n_hot <= 0) return MOE_ERR_UNSUPPORTED;
+  const FfnLayout L = ffn_layout(w, T, k);
+  const int S = ffn_slots(w, L, ws_bytes);
+  if (S < 1) return MOE_ERR_WORKSPACE;
+  const size_t R = (size_t)T * k;
+  switch (region) {
+    case MOE_WS_XQ: *offset = L.xq_off; *bytes = (size_t)T * w->H; break;
+    case MOE_WS_XQ_SCALES: *offset = L.xqs_off; *bytes = (size_t)T * (w->H / 32); break;
+    case MOE_WS_HQ: *offset = L.hq_off; *bytes = R * w->I; break;
+    case MOE_WS_HQ_SCALES: *offset = L.hqs_off; *bytes = R * (w->I / 32); break;
+    default: *offset = L.slots_off; *bytes = (size_t)S * L.slot_bytes; break;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_fp8_slot_layout(int32_t H, int32_t I, size_t* w1, size_t* w1_scales, size_t* w2,
+                               size_t* w2_scales, size_t* slot_bytes) {
+  if (H < 32 || I < 32 || H % 32 || I % 32 || !w1 || !w1_scales || !w2 || !w2_scales || !slot_bytes)
+    return MOE_ERR_INVALID_ARG;
+  const HotLayout L = hot_layout(H, I);
+  *w1 = (size_t)L.w1_off;
+  *w1_scales = (size_t)L.w1s_off;
+  *w2 = (size_t)L.w2_off;
+  *w2_scales = (size_t)L.w2s_off;
+  *slot_bytes = (size_t)L.slot_bytes;
+  return MOE_OK;
 }
 
 }  // extern "C"

@@ -116,11 +116,13 @@ struct ConvertJob {
 __global__ __launch_bounds__(256) void mxfp4_convert_kernel(ConvertJob j1, ConvertJob j2, int two,
                                                             const int32_t* __restrict__ hot_ids,
                                                             const int32_t* __restrict__ counts,
-                                                            int n_hot, int b0, int64_t slot_bytes) {
+                                                            int n_hot, int E, int b0, int64_t slot_bytes) {
   const int sl = blockIdx.y;
   const int s = b0 + sl;
   if (hot_ids) {
-    if (s >= n_hot || counts[hot_ids[s]] == 0) return;
+    if (s >= n_hot) return;
+    const int he = hot_ids[s];
+    if ((unsigned)he >= (unsigned)E || counts[he] == 0) return;  // invalid ids convert nothing
   }
   const bool second = two && blockIdx.z == 1;
   const ConvertJob& J = second ? j2 : j1;
@@ -148,7 +150,7 @@ hipError_t launch_mxfp4_to_fp8(const uint8_t* codes, const uint8_t* scales, int6
   if (j.n16 == 0) return hipSuccess;
   const int64_t want = (j.n16 + 255) / 256;
   const unsigned gx = (unsigned)(want < 4096 ? want : 4096);
-  mxfp4_convert_kernel<<<dim3(gx, 1, 1), 256, 0, s>>>(j, j, 0, nullptr, nullptr, 0, 0, 0);
+  mxfp4_convert_kernel<<<dim3(gx, 1, 1), 256, 0, s>>>(j, j, 0, nullptr, nullptr, 0, 0, 0, 0);
   return hipGetLastError();
 }
 
@@ -393,7 +395,7 @@ hipError_t launch_hot_convert(const HotWeights& hw, int H, int I, const int32_t*
   const int nb = hw.n_hot - b0 < S ? hw.n_hot - b0 : S;
   if (nb <= 0) return hipSuccess;
   // ~64 K threads per matrix and slot
-  mxfp4_convert_kernel<<<dim3(256, nb, 2), 256, 0, s>>>(j1, j2, 1, hw.hot_ids, counts, hw.n_hot, b0,
+  mxfp4_convert_kernel<<<dim3(256, nb, 2), 256, 0, s>>>(j1, j2, 1, hw.hot_ids, counts, hw.n_hot, hw.E, b0,
                                                         L.slot_bytes);
   return hipGetLastError();
 }

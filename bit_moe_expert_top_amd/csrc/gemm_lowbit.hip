@@ -392,4 +392,54 @@ hipError_t launch_lowbit_gemm_fc2(const LowbitWeights& w, int H, int I, int k,
   return hipErrorInvalidValue;
 }
 
+// ------------------------------------------------------------------ debug decode
+// One thread per (row, 32-k field): the field loader, table32 and decode32 of the grouped GEMM
+// (operand op of a field holds its k-slots 8 op .. 8 op + 7), written in natural k order.
+template <class F>
+__global__ __launch_bounds__(256) void debug_dequant_gemm_kernel(const uint8_t* __restrict__ codes,
+                                                                 const uint8_t* __restrict__ scales, int rows,
+                                                                 int K, float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int fpr = K / 32;
+  if (i >= (int64_t)rows * fpr) return;
+  const int row = (int)(i / fpr), f = (int)(i - (int64_t)row * fpr);
+  const uint32_t cbr = F::code_bytes((uint32_t)K), sbr = F::scale_bytes((uint32_t)K);
+  const buf_rsrc rc = make_rsrc(codes, (uint32_t)rows * cbr);
+  const buf_rsrc rs = make_rsrc(scales, (uint32_t)rows * sbr);
+  Field<F> g;
+  load_field<F>(g, rc, rs, (uint32_t)row * cbr + F::code_bytes(32u * f), (uint32_t)row * sbr + F::scale_bytes(32u * f));
+  const typename F::Tab tab = F::table32(g.s);
+  float* o = out + (int64_t)row * K + 32 * f;
+#pragma unroll
+  for (int op = 0; op < 4; ++op) {
+    const u32x4 v = F::decode32(g.c, tab, op);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int slot = 8 * op + 2 * d;
+      o[F::slot_k(slot)] = bf16_to_f32(v[d] & 0xFFFFu);
+      o[F::slot_k(slot + 1)] = bf16_to_f32(v[d] >> 16);
+    }
+  }
+}
+
+hipError_t launch_debug_dequant_gemm(const LowbitWeights& w, int H, int I, int e, int which, float* out,
+                                     hipStream_t s) {
+  const int rows = which == 1 ? 2 * I : H;
+  const int K = which == 1 ? H : I;
+  const uint8_t* codes = (const uint8_t*)(which == 1 ? w.w1_codes : w.w2_codes);
+  const uint8_t* scales = (const uint8_t*)(which == 1 ? w.w1_scales : w.w2_scales);
+  const int64_t n = (int64_t)rows * (K / 32);
+  const unsigned grid = (unsigned)((n + 255) / 256);
+  if (w.fmt == W2Fmt::kId) {
+    const size_t cb = (size_t)e * rows * W2Fmt::code_bytes(K), sb = (size_t)e * rows * W2Fmt::scale_bytes(K);
+    debug_dequant_gemm_kernel<W2Fmt><<<grid, 256, 0, s>>>(codes + cb, scales + sb, rows, K, out);
+  } else if (w.fmt == W3Fmt::kId) {
+    const size_t cb = (size_t)e * rows * W3Fmt::code_bytes(K), sb = (size_t)e * rows * W3Fmt::scale_bytes(K);
+    debug_dequant_gemm_kernel<W3Fmt><<<grid, 256, 0, s>>>(codes + cb, scales + sb, rows, K, out);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace bitmoe

@@ -64,6 +64,7 @@ hipError_t launch_lowbit_gemm_fc2(const LowbitWeights& w, int H, int I, int k,
 
 // ---- hot experts (MXFP4 held, converted to FP8 into workspace slots, MXFP8 activations)
 struct HotWeights {
+  int E;  // experts of the layer (hot ids outside [0, E) are ignored)
   int n_hot;
   const int32_t* hot_ids;
   const uint8_t* w1_codes;   // [n_hot][2I][H/2]
@@ -103,5 +104,8 @@ hipError_t launch_hot_fc2(int H, int I, int64_t R, const int32_t* hot_plan, int 
 
 hipError_t launch_debug_dequant(const LowbitWeights& w, int E, int H, int I, int e, int which,
                                 float* out, hipStream_t s);
+// The same through the grouped GEMM's field decoder (F::table32 / F::decode32).
+hipError_t launch_debug_dequant_gemm(const LowbitWeights& w, int H, int I, int e, int which, float* out,
+                                     hipStream_t s);
 
 }  // namespace bitmoe

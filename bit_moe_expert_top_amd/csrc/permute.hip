@@ -42,7 +42,7 @@ __device__ __forceinline__ void wave_pass(const int32_t* __restrict__ ids, int l
     const uint64_t m = match_lanes(key, nbits);
     const int rank = __popcll(m & below);
     const int n = __popcll(m);
-    if (key < E) {
+    if ((unsigned)key < (unsigned)E) {  // ids outside [0, E) are skipped (no LDS access)
       const int start = cnt[key];
       if (ASSIGN) {
         perm[start + rank] = r;

@@ -16,7 +16,10 @@ __device__ __forceinline__ void build_plan(const int32_t* __restrict__ offsets, 
   __shared__ int16_t slot_of[1024];
   for (int e = threadIdx.x; e < E; e += 1024) slot_of[e] = -1;
   __syncthreads();
-  for (int s = threadIdx.x; s < n_hot; s += 1024) slot_of[hot_ids[s]] = (int16_t)s;
+  for (int s = threadIdx.x; s < n_hot; s += 1024) {
+    const int he = hot_ids[s];
+    if ((unsigned)he < (unsigned)E) slot_of[he] = (int16_t)s;  // ids outside [0, E) are ignored
+  }
   __syncthreads();
   int4* items = reinterpret_cast<int4*>(plan + 4);
   int running = 0;
@@ -55,7 +58,10 @@ __device__ __forceinline__ void build_plan2(const int32_t* __restrict__ offsets,
   __shared__ int16_t slot_of[1024];
   for (int e = threadIdx.x; e < E; e += 1024) slot_of[e] = -1;
   __syncthreads();
-  for (int s = threadIdx.x; s < n_hot; s += 1024) slot_of[hot_ids[s]] = (int16_t)s;
+  for (int s = threadIdx.x; s < n_hot; s += 1024) {
+    const int he = hot_ids[s];
+    if ((unsigned)he < (unsigned)E) slot_of[he] = (int16_t)s;  // ids outside [0, E) are ignored
+  }
   __syncthreads();
   int4* items_s = reinterpret_cast<int4*>(plan_s + 4);
   int4* items_g = reinterpret_cast<int4*>(plan_g + 4);

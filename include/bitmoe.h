@@ -60,14 +60,14 @@ typedef enum {
  *
  *  MOE_FMT_W2    [Moet-QA] 2-bit codebook: codes u32[rows][K/16], code i of a word at bits
  *                [2i, 2i+2), code c -> level {-4,-1,1,4}[c]; scales bf16 (u16 bits)
- *                [rows][K/32]; weight = level * scale.  K % 256 == 0.
+ *                [rows][K/32]; weight = level * scale.  K a multiple of 32.
  *                Precondition: scales are normal bf16 numbers with |scale| < 2^125 (then the
  *                decoded weights are exact bf16 values; a zero or subnormal scale decodes the
  *                +-4 levels within 2^-124 of the exact value).
  *  MOE_FMT_W3    [Strata-R9700] 3-bit, 8 levels: codes u32[rows][K/32*3], the three words of a
  *                group of 32 codes form one little-endian 96-bit field and code i sits at bits
  *                [3i, 3i+3); code c -> level {-8,-5,-3,-1,1,3,5,8}[c]; scales e4m3fn bytes
- *                [rows][K/64]; weight = level * e4m3(scale) / 64.  K % 256 == 0.
+ *                [rows][K/64]; weight = level * e4m3(scale) / 64.  K a multiple of 64.
  *  MOE_FMT_MXFP4 [OCP-MX] e2m1 elements, codes u8[rows][K/2] (element 2i in the low nibble),
  *                e8m0 scale bytes [rows][K/32]; weight = e2m1 * 2^(scale-127).  Hot set only.
  */
@@ -113,7 +113,11 @@ typedef struct {
 moe_status moe_route(const float* logits, int32_t T, int32_t E, int32_t k,
                      int32_t* topk_ids, float* topk_w, void* stream);
 
-/* moe_permute -- stable grouping of the R = T*k routed rows by expert.
+/* moe_permute -- stable grouping of the R = T*k routed rows by expert.  Plain reading: the pages
+ * compute the routed experts of a step expert by expert ([Moet-README], README tables of the
+ * hybrid: the routed experts of every layer, each computed where it is held) but do not describe
+ * how rows are grouped; this is the plainest grouping that lets one kernel pass handle one
+ * expert's rows together.
  *   topk_ids i32[T][k]    expert of row t*k+j (values in [0, E))
  *   counts   i32[E]       out: rows routed to each expert
  *   offsets  i32[E+1]     out: exclusive prefix sum of counts (offsets[E] = R)
@@ -145,9 +149,11 @@ moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
  *            the largest that fits in ws_bytes, capped at n_hot, and the hot experts are
  *            converted and computed in batches of that many (at least one slot must fit).
  *   hot_ids  must be distinct expert ids in [0, E) (not checked: device memory).
- * Requirements: H % 256 == 0, I % 256 == 0, H and I <= 16384; fmt W2 or W3; T * H * 2 < 2^32
- * (x is addressed with 32-bit byte offsets; larger batches return UNSUPPORTED: split them).
- * Errors: INVALID_ARG, UNSUPPORTED (format/shape not built), WORKSPACE. */
+ * Shapes: H and I must be whole scale groups (multiples of 32; of 64 for W3), else INVALID_ARG.
+ * The kernels are built for H % 256 == 0, I % 256 == 0 and H, I <= 16384: other valid shapes
+ * return UNSUPPORTED.  fmt W2 or W3.  T * H * 2 < 2^32 (x is addressed with 32-bit byte offsets;
+ * larger batches return UNSUPPORTED: split them).
+ * Errors: INVALID_ARG, UNSUPPORTED (a valid format/shape the kernels are not built for), WORKSPACE. */
 size_t moe_expert_ffn_ws_bytes(const moe_weights* w, int32_t T, int32_t k, int32_t fp8_slots);
 moe_status moe_expert_ffn(const moe_weights* w, const uint16_t* x, int32_t T, int32_t k,
                           const int32_t* counts, const int32_t* offsets, const int32_t* perm,
@@ -171,8 +177,43 @@ moe_status moe_expert_ffn_stage(const moe_weights* w, const uint16_t* x, int32_t
                                 float* y_perm, void* ws, size_t ws_bytes, int32_t stage,
                                 void* stream);
 
+/* moe_expert_ffn_ws_region -- where an intermediate result of moe_expert_ffn lives in its
+ * workspace, so that a test can read it back after the stage that writes it (the pages check a
+ * conversion by comparing its output on fixed inputs: [Day0-MXFP4] section 4, the consistency
+ * check after the online conversion).  For the same (w, T, k, ws_bytes) as the FFN call:
+ *   MOE_WS_XQ          u8[T][H]     MXFP8 elements of x (stage 5, hot set only)
+ *   MOE_WS_XQ_SCALES   u8[T][H/32]  their e8m0 scales
+ *   MOE_WS_HQ          u8[R][I]     MXFP8 h of the rows of hot experts (row r = grouped row r,
+ *                                   columns in natural order), written by the FP8 FC1 stage of
+ *                                   the batch that holds the row's expert; other rows untouched
+ *   MOE_WS_HQ_SCALES   u8[R][I/32]  their e8m0 scales
+ *   MOE_WS_SLOTS       the S FP8 slots, S * slot_bytes (see moe_fp8_slot_layout): slot j holds
+ *                      the converted image of hot expert b0 + j of the current batch, written by
+ *                      that batch's convert stage only if the expert has rows
+ * *offset and *bytes receive the region's byte offset in ws and its size.
+ * Errors: INVALID_ARG (bad weights or sizes, unknown region, null outputs), UNSUPPORTED (a hot
+ * region without a hot set), WORKSPACE (ws_bytes too small for the call). */
+typedef enum {
+  MOE_WS_XQ = 1,
+  MOE_WS_XQ_SCALES = 2,
+  MOE_WS_HQ = 3,
+  MOE_WS_HQ_SCALES = 4,
+  MOE_WS_SLOTS = 5
+} moe_ws_region;
+moe_status moe_expert_ffn_ws_region(const moe_weights* w, int32_t T, int32_t k, size_t ws_bytes,
+                                    int32_t region, size_t* offset, size_t* bytes);
+
+/* moe_fp8_slot_layout -- byte layout of one FP8 slot ([Day0-MXFP4] section 4: the converted
+ * image of one MXFP4 expert): W1 e4m3fn elements u8[2I][H] at *w1, their e8m0 scales
+ * u8[2I][H/32] at *w1_scales, W2 elements u8[H][I] at *w2, scales u8[H][I/32] at *w2_scales
+ * (offsets from the slot's start), and the slot size (the stride between slots).
+ * Errors: INVALID_ARG (H or I not positive multiples of 32, null outputs). */
+moe_status moe_fp8_slot_layout(int32_t H, int32_t I, size_t* w1, size_t* w1_scales, size_t* w2,
+                               size_t* w2_scales, size_t* slot_bytes);
+
 /* moe_combine -- out[t] = sum over j = 0..k-1 (in that order) of topk_w[t][j] * y_perm[inv[t*k+j]],
- * accumulated in fp32.  out is f32[T][H] if out_is_fp32, else bf16 (u16 bits, round to
+ * accumulated in fp32.  Plain reading: the pages do not describe the combine; this is the
+ * gate-weighted sum of a token's routed-expert outputs that the gates of moe_route define.  out is f32[T][H] if out_is_fp32, else bf16 (u16 bits, round to
  * nearest even of the same fp32 sum).
  * Errors: INVALID_ARG. */
 moe_status moe_combine(const float* y_perm, const int32_t* inv, const float* topk_w,
@@ -273,7 +314,9 @@ moe_status moe_tier_remap(const int32_t* topk_ids, int64_t R, const int32_t* slo
 /* moe_debug_dequant -- decode one low-bit expert matrix with the same device code the FFN
  * kernels use, into f32[rows][K] (W1: rows = 2I, K = H; W2: rows = H, K = I), in natural K
  * order.  For tests: the decoded weights must equal the format definition bit for bit.
- *   which: 1 (W1) or 2 (W2).   Errors: INVALID_ARG, UNSUPPORTED. */
+ *   which: 1 (W1) or 2 (W2) through the weight-streaming kernels' decoder; 3 (W1) or 4 (W2)
+ *          through the grouped-GEMM kernels' decoder (one 32-k field per lane).
+ * Errors: INVALID_ARG, UNSUPPORTED. */
 moe_status moe_debug_dequant(const moe_weights* w, int32_t e, int32_t which, float* out,
                              void* stream);
 

@@ -76,7 +76,15 @@ def test_ffn_argument_checks(lib):
     w = L.MoeWeights(8, 256, 512, L.MOE_FMT_W2, p, p, p, p, 0, None, None, None, None, None)
     assert L.lib.moe_expert_ffn_ws_bytes(ctypes.byref(w), 16, 2, 0) > 0
     bad = L.MoeWeights(8, 200, 512, L.MOE_FMT_W2, p, p, p, p, 0, None, None, None, None, None)
-    assert L.lib.moe_expert_ffn(ctypes.byref(bad), p, 16, 2, p, p, p, p, p, 1 << 30, None) == -1  # H % 256
+    assert L.lib.moe_expert_ffn(ctypes.byref(bad), p, 16, 2, p, p, p, p, p, 1 << 30, None) == -1  # H % 32
+    # whole scale groups (32 weights, 64 for 3-bit) but not whole 256-k steps: valid, not built
+    for fmt, H, want in ((L.MOE_FMT_W2, 288, -2), (L.MOE_FMT_W3, 288, -1), (L.MOE_FMT_W3, 320, -2),
+                         (L.MOE_FMT_W2, 20480, -2)):
+        wh = L.MoeWeights(8, H, 512, fmt, p, p, p, p, 0, None, None, None, None, None)
+        assert L.lib.moe_expert_ffn(ctypes.byref(wh), p, 16, 2, p, p, p, p, p, 1 << 30, None) == want, (fmt, H)
+        wi = L.MoeWeights(8, 512, H, fmt, p, p, p, p, 0, None, None, None, None, None)
+        assert L.lib.moe_expert_ffn(ctypes.byref(wi), p, 16, 2, p, p, p, p, p, 1 << 30, None) == want, (fmt, H)
+        assert L.lib.moe_expert_ffn_ws_bytes(ctypes.byref(wh), 16, 2, 0) == 0
     assert L.lib.moe_expert_ffn(ctypes.byref(w), p, 16, 2, p, p, p, p, p, 10, None) == -3  # workspace
     nofmt = L.MoeWeights(8, 256, 512, 7, p, p, p, p, 0, None, None, None, None, None)
     assert L.lib.moe_expert_ffn(ctypes.byref(nofmt), p, 16, 2, p, p, p, p, p, 1 << 30, None) == -1

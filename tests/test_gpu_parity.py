@@ -9,8 +9,8 @@ import moegen
 from oracle import formats as OF
 from oracle import moe as OM
 
-from _helpers import (TOL_BF16, TOL_FP8, bf16_bits_host, device_layer, host, layer_arrays, max_err_over_rms,
-                      oracle_layer, to_dev)
+from _helpers import (TOL_BF16, TOL_FP8, device_layer, host, max_err_over_rms, oracle_layer, oracle_token_rows,
+                      sample_tokens, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -29,12 +29,14 @@ def L():
                                                    ("w3", [0, 3, 15], {"E": 16}),
                                                    ("w3", [2, 7], {"E": 8, "k": 2, "H": 256, "I": 512})])
 def test_debug_dequant_bit_exact(L, name, experts, override):
+    """Both decoders (which 1, 2: the weight-streaming kernels'; 3, 4: the grouped GEMM's field
+    decoder) give the format's weights bit for bit."""
     sp, dw = device_layer(name, **override)
     lay = oracle_layer(name, **override)
     for e in experts:
-        for which in (1, 2):
+        for which in (1, 2, 3, 4):
             got = host(L.moe_debug_dequant(dw, e, which)).astype(np.float64)
-            want = lay.dense(e, which)
+            want = lay.dense(e, 1 if which in (1, 3) else 2)
             assert np.array_equal(got, want), (name, e, which, np.argwhere(got != want)[:5])
 
 
@@ -91,7 +93,10 @@ def test_combine_bf16_is_rne_of_fp32(L):
 
 
 # ------------------------------------------------------------------ the whole layer
-def _check_layer(L, name, T, sample_tokens=None, fp8_slots=None, **override):
+def _check_layer(L, name, T, sample=False, fp8_slots=None, **override):
+    """The whole layer against the oracle: routing and grouping over every token, bit for bit;
+    float outputs of every token, or (sample=True) of 256 seeded tokens (their k routed rows
+    each: the expert outputs y_perm and the combined output), within the tolerance."""
     sp, dw = device_layer(name, **override)
     lay = oracle_layer(name, **override)
     b = moegen.batch(sp, T)
@@ -105,16 +110,25 @@ def _check_layer(L, name, T, sample_tokens=None, fp8_slots=None, **override):
     np.testing.assert_array_equal(host(res["offsets"]), offsets)
     np.testing.assert_array_equal(host(res["perm"]), perm)
     np.testing.assert_array_equal(host(res["inv"]), inv)
-    toks = np.arange(T) if sample_tokens is None else np.asarray(sample_tokens)
-    experts = sorted(set(ids[toks].reshape(-1).tolist()))
-    y = OM.expert_ffn(lay, b["x"], k, offsets, perm, experts=experts)
-    out = OM.combine(np.nan_to_num(y), inv, gates, T, k)[toks]
+    if sample:
+        toks = sample_tokens(T)
+        yt = oracle_token_rows(lay, b["x"], ids, toks, k)
+        rows = np.array([inv[t * k + j] for t in toks for j in range(k)])
+        y_rows = np.stack([yt[(int(t), j)] for t in toks for j in range(k)])
+        out = np.zeros((len(toks), sp["H"]))
+        for j in range(k):
+            out += gates[toks, j:j + 1] * np.stack([yt[(int(t), j)] for t in toks])
+    else:
+        toks = np.arange(T)
+        y = OM.expert_ffn(lay, b["x"], k, offsets, perm)
+        out = OM.combine(y, inv, gates, T, k)
+        rows = np.arange(T * k)
+        y_rows = y
     got = host(res["out"])[toks]
     err = max_err_over_rms(got, out)
-    print(f"{name} T={T}: max|err|/rms = {err:.4g}", flush=True)
+    print(f"{name} T={T}: {len(toks)} tokens, max|err|/rms = {err:.4g}", flush=True)
     assert err <= tol
-    rows = np.concatenate([np.arange(offsets[e], offsets[e + 1]) for e in experts])
-    assert max_err_over_rms(host(res["y_perm"])[rows], y[rows]) <= tol
+    assert max_err_over_rms(host(res["y_perm"])[rows], y_rows) <= tol
     # bf16 output is the RNE of the same fp32 sums
     o16 = L.moe_combine(res["y_perm"], res["inv"], res["gates"], out_fp32=False)
     ref16 = res["out"].to(torch.bfloat16).view(torch.int16)
@@ -156,19 +170,18 @@ def test_ffn_repeated_expert_ids(L, T):
     assert err <= TOL_BF16
 
 
-@pytest.mark.parametrize("T,sample", [(1, None), (8, None), (64, [0, 31, 63])])
-def test_layer_decode(L, T, sample):
-    _check_layer(L, "decode", T, sample)
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_layer_decode(L, T):
+    _check_layer(L, "decode", T)
 
 
-@pytest.mark.parametrize("T,sample", [(256, [0, 100, 255])])
-def test_layer_decode_shape_gemm_path(L, T, sample):
-    _check_layer(L, "decode", T, sample)
+def test_layer_decode_shape_gemm_path(L):
+    _check_layer(L, "decode", 256, sample=True)
 
 
-@pytest.mark.parametrize("T,sample", [(8192, [0, 4097, 8191]), (65536, [0, 32768, 65535])])
-def test_layer_prefill(L, T, sample):
-    _check_layer(L, "prefill", T, sample)
+@pytest.mark.parametrize("T", [8192, 65536])
+def test_layer_prefill(L, T):
+    _check_layer(L, "prefill", T, sample=True)
 
 
 # 3-bit experts: a small variant (many T, both kernels) and the full 512-expert shape
@@ -180,8 +193,7 @@ def test_layer_w3_small(L, T):
     _check_layer(L, "w3", T, **W3_SMALL)
 
 
-@pytest.mark.parametrize("T,sample", [(1, None), (8, None), (64, [0, 17, 63]), (512, [0, 255, 511]),
-                                      (4096, [0, 2048, 4095])])
+@pytest.mark.parametrize("T,sample", [(1, False), (8, False), (64, False), (512, True), (4096, True)])
 def test_layer_w3(L, T, sample):
     _check_layer(L, "w3", T, sample)
 
@@ -207,7 +219,7 @@ def test_mxfp8_quantize_bit_exact(L):
     x[1, :32] = r.integers(1, 0x80, 32)             # bf16 subnormals
     x[1, 32:64] = 0x7F7F                            # the largest bf16
     x[2, :32] = moegen._f32_to_bf16_bits(np.float32(1.8125) * np.ones(32, np.float32))  # ties at the top
-    x[2, 40] = moegen._f32_to_bf16_bits(np.float32(-448.0 * 1.0625))
+    x[2, 40] = moegen._f32_to_bf16_bits(np.array([-448.0 * 1.0625], np.float32))[0]
     x[3, :] = moegen._f32_to_bf16_bits(np.float32(1e-3) * r.standard_normal(K).astype(np.float32))
     elems, sc = L.moe_mxfp8_quantize(to_dev(x))
     we, ws = OF.mxfp8_quantize(OF.bf16_value(x))
@@ -229,7 +241,7 @@ def test_layer_mixed_small_fewer_slots_than_hot_experts(L):
     assert torch.equal(a["out"], b["out"])
 
 
-@pytest.mark.parametrize("T,sample", [(64, [0, 31, 63]), (4096, [0, 1500, 4095])])
+@pytest.mark.parametrize("T,sample", [(64, False), (4096, True)])
 def test_layer_mixed(L, T, sample):
     _check_layer(L, "mixed", T, sample)
 

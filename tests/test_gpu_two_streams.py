@@ -1,6 +1,6 @@
 """GPU: moe_expert_ffn with the hot experts' preparation and MXFP4 -> FP8 conversion on a
-second stream, concurrent with the low-bit stages ([Moet-QA]: converting the next experts while
-the current ones compute).  Same kernels on the same inputs: the output must be bit-equal to the
+second stream, concurrent with the low-bit stages ([Day0-MXFP4] section 4: the conversion of the next
+experts runs on another stream while the current ones compute).  Same kernels on the same inputs: the output must be bit-equal to the
 one-stream call, eagerly and replayed from a HIP graph."""
 import pytest
 import torch

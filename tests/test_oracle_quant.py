@@ -161,3 +161,73 @@ def test_mxfp4_round_trip_and_quality():
     w = (rng.standard_normal((32, 512)) * 0.02).astype(np.float32)
     d = F.dequant_mxfp4(*Q.quantize_mxfp4(w))
     assert float(np.sum(d * w) / np.linalg.norm(d) / np.linalg.norm(w)) > 0.98
+
+
+def _bf16_rne_fp64(v):
+    """fp64 -> nearest bf16 value (8 significant bits, ties to even), computed from the
+    exponent and np.round (half to even) rather than from bit patterns."""
+    v = np.asarray(v, dtype=np.float64)
+    out = np.zeros_like(v)
+    nz = v != 0
+    e = np.floor(np.log2(np.abs(v[nz])))
+    ulp = np.exp2(e - 7)
+    out[nz] = np.round(v[nz] / ulp) * ulp
+    return out
+
+
+def _w2_chain_fp64(g, rounds):
+    """The fit written independently of the oracle: brute-force nearest level (argmin over the
+    four levels) and a least-squares scale from numpy's lstsq, in fp64, `rounds` times from
+    s = max|w| / 4.  Returns the last scale, the last codes and the smallest relative distance
+    of any weight to a decision threshold over the rounds (to set aside near-ties)."""
+    lev = np.array([-4.0, -1.0, 1.0, 4.0])
+    gd = g.astype(np.float64)
+    s = np.max(np.abs(gd), axis=1) / 4.0
+    c = None
+    margin = np.full(len(g), np.inf)
+    for _ in range(rounds):
+        d = np.abs(gd[..., None] - lev * s[:, None, None])
+        c = np.argmin(d, axis=-1)
+        ds = np.sort(d, axis=-1)
+        margin = np.minimum(margin, np.min((ds[..., 1] - ds[..., 0]) / np.abs(s)[:, None], axis=1))
+        s = np.array([np.linalg.lstsq(lev[c[i]][:, None], gd[i], rcond=None)[0][0] for i in range(len(g))])
+    return s, c, margin
+
+
+def test_w2_stored_scale_and_final_codes_against_an_independent_fit():
+    """quantize_w2 returns (a) the bf16 (nearest even) of the least-squares scale refitted on the
+    codes of round 3, and (b) codes that are the nearest levels of w against that *stored* bf16
+    scale.  Both are checked against a fit written here from brute force and lstsq, and the data
+    is chosen so that two or four rounds, or keeping round 3's codes, would give other results."""
+    rng = np.random.default_rng(9)
+    G = 3000
+    base = rng.standard_normal((G, 32))
+    heavy = rng.standard_t(2.0, size=(G, 32))            # heavy tails: rounds keep moving codes
+    g = np.where(rng.uniform(size=(G, 1)) < 0.5, base, heavy) * rng.uniform(0.005, 0.05, (G, 1))
+    g = g.astype(np.float32)
+    codes, scales = Q.quantize_w2(g)
+    got_s = F.bf16_value(scales.reshape(-1))
+    got_c = _codes_of(codes.reshape(G, 2))
+    lev = np.array([-4.0, -1.0, 1.0, 4.0])
+    s3, c3, margin = _w2_chain_fp64(g, 3)
+    want_s = _bf16_rne_fp64(s3)
+    # set aside groups where fp32 and fp64 arithmetic could round a decision differently: a weight
+    # within 1e-5 (relative to s) of a threshold in some round, or s3 near a bf16 rounding midpoint
+    e = np.floor(np.log2(np.abs(s3)))
+    frac = np.abs(s3) / np.exp2(e - 7)
+    near_mid = np.abs(frac - np.floor(frac) - 0.5) < 1e-4
+    keep = (margin > 1e-5) & ~near_mid
+    assert keep.mean() > 0.99
+    assert np.array_equal(got_s[keep], want_s[keep])
+    # (b) final codes: brute-force nearest level against the stored scale
+    d = np.abs(g.astype(np.float64)[..., None] - lev * got_s[:, None, None])
+    ds = np.sort(d, axis=-1)
+    clear = np.min(ds[..., 1] - ds[..., 0], axis=1) > 0   # no exact tie in the group
+    assert clear.mean() > 0.99
+    assert np.array_equal(got_c[clear], np.argmin(d, axis=-1)[clear])
+    # the pin's power: on this data the round count and the final reassignment both matter
+    s2, _, _ = _w2_chain_fp64(g, 2)
+    s4, _, _ = _w2_chain_fp64(g, 4)
+    assert np.sum(_bf16_rne_fp64(s2)[keep] != want_s[keep]) > 10
+    assert np.sum(_bf16_rne_fp64(s4)[keep] != want_s[keep]) > 10
+    assert np.sum(np.any(c3 != got_c, axis=1)) > 10
