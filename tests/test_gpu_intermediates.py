@@ -114,16 +114,75 @@ def test_fp8_slot_image_bit_exact(L, fp8_slots):
 
 
 def _hq_oracle(lay, x_bits, k, I, rows, perm, offsets):
-    """MXFP8 of the oracle's h for the given grouped rows of hot experts: x quantised to MXFP8,
-    FC1 with the expert's FP8 image, SwiGLU, all in fp64, then MXFP8."""
+    """The oracle's h (fp64) for the given grouped rows of hot experts -- x quantised to MXFP8,
+    FC1 with the expert's FP8 image, SwiGLU -- and a first-order bound of how far a computation
+    whose FC1 sums carry an error of at most KAPPA * sqrt(sum of squared products) can move h:
+    |dh| <= |silu'(g)| |u| dg + |silu(g)| du."""
     X = OF.bf16_value(x_bits)
     Xq = OF.mxfp8_dequant(*OF.mxfp8_quantize(X))
     expert_of = np.searchsorted(offsets, rows, side="right") - 1
     h = np.zeros((len(rows), I))
+    dh = np.zeros((len(rows), I))
     for e in sorted(set(expert_of.tolist())):
         sel = np.nonzero(expert_of == e)[0]
-        h[sel] = OM.swiglu(OM.fc1(Xq[perm[rows[sel]] // k], lay.dense(e, 1)))
-    return OF.mxfp8_quantize(h)
+        xs = Xq[perm[rows[sel]] // k]
+        W1 = lay.dense(e, 1)
+        a = OM.fc1(xs, W1)
+        s = np.sqrt(OM.fc1(xs * xs, W1 * W1))
+        g, u = a[:, :I], a[:, I:]
+        sig = 1.0 / (1.0 + np.exp(-g))
+        h[sel] = OM.swiglu(a)
+        dsilu = sig * (1.0 + g * (1.0 - sig))
+        dh[sel] = KAPPA * (np.abs(dsilu * u) * s[:, :I] + np.abs(g * sig) * s[:, I:])
+    return h, dh
+
+
+# Reading of the h_q bar.  The matrix cores' FP8 dot products are not exact fp32 sums: one
+# v_mfma_scale_f32_32x32x64_f8f6f4 on random e4m3 operands deviated from the exact sum of its 64
+# products by up to 3.2e-4 of the rms of such sums (measured on the device), far above fp32
+# rounding.  So a value of h that close to an e4m3 rounding midpoint may round the other way:
+# measured on a few 1e-4 of the elements, not the 1e-4 an IEEE fp32 sum would give.  The test
+# bounds the rate at 1e-3 and checks that every difference is one the arithmetic explains: the
+# oracle's exact h lies within the error bound dh (KAPPA = 1e-3, three times the largest
+# deviation measured) of the values that round to the GPU's element.  A block scale may differ only where the oracle's amax lies within dh of a
+# power of two, and on at most 1e-4 of the blocks.
+HQ_RATE = 1e-3
+KAPPA = 1e-3
+
+
+def _e4m3_grid():
+    vals = OF.e4m3fn_value(np.arange(256, dtype=np.uint8))
+    return np.unique(vals[np.isfinite(vals)])
+
+
+def _check_hq(h, dh, hq, hqs):
+    """The h_q bar above; returns (element rate, differing elements, differing scales)."""
+    we, wsc = OF.mxfp8_quantize(h)
+    n, I = h.shape
+    # scales: the shared exponent follows floor(log2 amax); a difference needs amax next to 2^e
+    bad_s = hqs != wsc
+    hb, db = np.abs(h.reshape(n, I // 32, 32)), dh.reshape(n, I // 32, 32)
+    amax = np.max(hb, axis=-1)
+    slack = db[np.arange(n)[:, None], np.arange(I // 32)[None, :], np.argmax(hb, axis=-1)]
+    p2 = np.exp2(np.round(np.log2(np.where(amax > 0, amax, 1.0))))
+    assert bad_s.mean() <= 1e-4, bad_s.mean()
+    assert np.all(np.abs(amax - p2)[bad_s] <= slack[bad_s]), (amax[bad_s], slack[bad_s])
+    # elements of the blocks whose scales agree (-0 and +0 are the same value)
+    same = np.repeat(~bad_s, 32, axis=1)
+    bad_e = (OF.e4m3fn_value(hq) != OF.e4m3fn_value(we)) & same
+    rate = bad_e.sum() / max(1, same.sum())
+    assert rate <= HQ_RATE, rate
+    # the oracle's exact h must lie within dh of the interval of values that round to the GPU's
+    # element (between the midpoints to its neighbours; e4m3 saturates beyond +-448)
+    grid = _e4m3_grid()
+    sc = np.exp2(np.repeat(wsc.astype(np.float64) - 127.0, 32, axis=1))[bad_e]
+    gi = np.searchsorted(grid, OF.e4m3fn_value(hq[bad_e]))
+    lo = np.where(gi > 0, (grid[np.maximum(gi - 1, 0)] + grid[gi]) / 2, -np.inf) * sc
+    hi = np.where(gi < grid.size - 1, (grid[np.minimum(gi + 1, grid.size - 1)] + grid[gi]) / 2, np.inf) * sc
+    v = h[bad_e]
+    dist = np.maximum(lo - v, 0) + np.maximum(v - hi, 0)
+    assert np.all(dist <= dh[bad_e]), (dist / dh[bad_e]).max()
+    return rate, int(bad_e.sum()), int(bad_s.sum())
 
 
 @pytest.mark.parametrize("name,T,override,n_rows", [("mixed", 300, MIXED_SMALL, None), ("mixed", 64, {}, None),
@@ -142,18 +201,7 @@ def test_hq_matches_oracle(L, name, T, override, n_rows):
         rows = np.sort(np.random.default_rng(T).choice(rows, n_rows, replace=False))
     hq = _region(L, dw, T, k, ws, L.MOE_WS_HQ).reshape(T * k, I)[rows]
     hqs = _region(L, dw, T, k, ws, L.MOE_WS_HQ_SCALES).reshape(T * k, I // 32)[rows]
-    we, wsc = _hq_oracle(lay, b["x"], k, I, rows, perm, offsets)
-    bad_e = hq != we
-    bad_s = hqs != wsc
-    rate_e, rate_s = bad_e.mean(), bad_s.mean()
-    print(f"{name} T={T}: {rows.size} hot rows, h_q mismatches {bad_e.sum()} of {bad_e.size} ({rate_e:.2e}), "
-          f"scales {bad_s.sum()} of {bad_s.size} ({rate_s:.2e})", flush=True)
-    assert rate_e <= 1e-4 and rate_s <= 1e-4
-    # where the scale agrees, a differing element is the neighbouring e4m3 value of the oracle's
-    same_scale = np.repeat(~bad_s, 32, axis=1)
-    ge, oe = OF.e4m3fn_value(hq[bad_e & same_scale]), OF.e4m3fn_value(we[bad_e & same_scale])
-    codes = np.arange(256, dtype=np.uint8)
-    vals = OF.e4m3fn_value(codes)
-    finite = np.sort(np.unique(vals[np.isfinite(vals)]))
-    gi, oi = np.searchsorted(finite, ge), np.searchsorted(finite, oe)
-    assert np.all(np.abs(gi - oi) <= 1), list(zip(ge, oe))[:5]
+    h, dh = _hq_oracle(lay, b["x"], k, I, rows, perm, offsets)
+    rate, n_e, n_s = _check_hq(h, dh, hq, hqs)
+    print(f"{name} T={T}: {rows.size} hot rows, h_q elements differing {n_e} ({rate:.2e}), scales {n_s}",
+          flush=True)
