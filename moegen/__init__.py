@@ -16,6 +16,8 @@ decode    384     8   4096   2048   2-bit   Zipf(s=1.1) logits, T = 1 / 8 / 64
 prefill   384     8   4096   2048   2-bit   Zipf(s=1.1) logits, T = 8192 / 65536
 mixed     384     8   4096   2048   2-bit   hottest 32 experts held in MXFP4, T = 4096
 w3        512    10   2048    512   3-bit   Zipf(s=1.1) logits, T = 1 .. 4096
+residual  384     8   4096   2048   2-bit   hottest 32 experts carry an MXFP4 residual
+                                            (FP4 delta) on top of their 2-bit codes
 ========  =====  ===  =====  =====  ======  ============================================
 
 Storage layouts (all row-major, K = reduction dim is contiguous):
@@ -36,7 +38,9 @@ Draws:
   [0.0039, 0.0293] -- the same magnitude as the 2-bit scales, drawn as bytes so no
   e4m3 encoder is needed here.
 * MXFP4: uniform nibbles (uniform bytes); e8m0 scale bytes uniform in {120, 121}.
-* Hot set (mixed layer): the 32 experts of Zipf rank 1..32, hottest first.
+* MXFP4 residual (residual layer): uniform nibbles; e8m0 scale bytes uniform in {116, 117}
+  (2^-11, 2^-10: a correction about an order of magnitude below the 2-bit weights).
+* Hot set (mixed and residual layers): the 32 experts of Zipf rank 1..32, hottest first.
 
 Weights depend only on the layer (seed 1000 + layer index, then the expert id);
 activations and logits also depend on T, so one layer serves every batch size.
@@ -52,13 +56,18 @@ LAYERS = {
     "prefill": (2, 384, 8, 4096, 2048, "w2", 1.1, 0, (8192, 65536)),
     "mixed": (3, 384, 8, 4096, 2048, "w2", 1.1, 32, (4096,)),
     "w3": (4, 512, 10, 2048, 512, "w3", 1.1, 0, (1, 8, 64, 512, 4096)),
+    "residual": (5, 384, 8, 4096, 2048, "w2", 1.1, 32, (1, 8, 64)),
 }
+# how the hot set is held: "replace" (the hot experts are MXFP4 instead of low-bit) or
+# "residual" (their low-bit codes plus an MXFP4 residual)
+HOT_MODE = {"mixed": "replace", "residual": "residual"}
 
 
 def spec(name: str, **override) -> dict:
     """Shape and format of a layer as a dict; keyword overrides allow small variants."""
     idx, E, k, H, I, fmt, zipf, n_hot, Ts = LAYERS[name]
-    d = dict(name=name, index=idx, E=E, k=k, H=H, I=I, fmt=fmt, zipf=zipf, n_hot=n_hot, Ts=Ts)
+    d = dict(name=name, index=idx, E=E, k=k, H=H, I=I, fmt=fmt, zipf=zipf, n_hot=n_hot, Ts=Ts,
+             hot_mode=HOT_MODE.get(name, "replace"))
     d.update(override)
     return d
 
@@ -103,9 +112,10 @@ def _codes_scales(r: np.random.Generator, fmt: str, rows: int, K: int):
         man = r.integers(0, 8, size=(rows, K // 64), dtype=np.uint8)
         scales = ((sgn << 7) | (ex << 3) | man).astype(np.uint8)
         return codes, scales
-    if fmt == "mxfp4":
+    if fmt in ("mxfp4", "mxfp4res"):
         codes = r.integers(0, 256, size=(rows, K // 2), dtype=np.uint8)
-        scales = r.integers(120, 122, size=(rows, K // 32), dtype=np.uint8)
+        lo = 120 if fmt == "mxfp4" else 116
+        scales = r.integers(lo, lo + 2, size=(rows, K // 32), dtype=np.uint8)
         return codes, scales
     raise ValueError(fmt)
 
@@ -113,9 +123,9 @@ def _codes_scales(r: np.random.Generator, fmt: str, rows: int, K: int):
 def expert(sp: dict, e: int, fmt: str | None = None) -> dict:
     """Packed weights of one expert: w1_codes/w1_scales ([2I] rows, K=H) and
     w2_codes/w2_scales ([H] rows, K=I).  ``fmt`` defaults to the layer's low-bit
-    format; pass "mxfp4" for the hot-set copy of an expert."""
+    format; pass "mxfp4" for the hot-set copy of an expert, "mxfp4res" for its residual."""
     fmt = fmt or sp["fmt"]
-    stream = {"w2": 1, "w3": 1, "mxfp4": 2}[fmt]
+    stream = {"w2": 1, "w3": 1, "mxfp4": 2, "mxfp4res": 4}[fmt]
     r = _rng(1000 + sp["index"], stream, e)
     H, I = sp["H"], sp["I"]
     c1, s1 = _codes_scales(r, fmt, 2 * I, H)
@@ -136,11 +146,12 @@ def weights(sp: dict) -> dict:
     hid = hot_ids(sp)
     out["hot_ids"] = hid
     if len(hid):
-        h0 = expert(sp, int(hid[0]), "mxfp4")
+        hf = "mxfp4res" if sp.get("hot_mode") == "residual" else "mxfp4"
+        h0 = expert(sp, int(hid[0]), hf)
         for key, a in h0.items():
             out["hot_" + key] = np.empty((len(hid),) + a.shape, a.dtype)
         for s, e in enumerate(hid):
-            for key, a in expert(sp, int(e), "mxfp4").items():
+            for key, a in expert(sp, int(e), hf).items():
                 out["hot_" + key][s] = a
     return out
 

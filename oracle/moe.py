@@ -102,29 +102,51 @@ class Layer:
 
     ``arrays`` holds the low-bit stacks (``w1_codes`` ... ``w2_scales`` with a leading
     [E] axis) and optionally ``hot_ids`` plus the MXFP4 stacks (``hot_w1_codes`` ...).
-    ``fmt`` is "w2" or "w3".  A hot expert is held in MXFP4 and computed in FP8 after
-    the conversion of [Day0-MXFP4] section 4; every other expert in the low-bit format
-    (reading: the hot set *replaces* the low-bit copy of those experts)."""
+    ``fmt`` is "w2" or "w3".  ``hot_mode`` says what the MXFP4 stacks of the hot set are:
 
-    def __init__(self, fmt: str, arrays: dict):
+    * "replace": a hot expert is held in MXFP4 and computed in FP8 after the conversion of
+      [Day0-MXFP4] section 4; its low-bit copy is not used (reading: the hot set *replaces*
+      the low-bit copy of those experts);
+    * "residual": [Moet-QA] (the FP4 delta cache: the hottest experts get an FP4-precision
+      correction layer above their 2-bit weights) and [Moet-README] README line "2-bit
+      experts on vLLM v0.24.0" (a 2-bit codebook plus an FP4 delta cache).  Reading: a hot
+      expert's weight is its 2-bit weight plus the MXFP4 residual, summed element by element
+      before the matmuls (so before SwiGLU), and computed like the 2-bit experts (bf16
+      operands; the sum is formed exactly here in fp64)."""
+
+    def __init__(self, fmt: str, arrays: dict, hot_mode: str = "replace"):
+        assert hot_mode in ("replace", "residual")
+        assert hot_mode == "replace" or fmt == "w2", "the FP4 residual sits on 2-bit experts"
         self.fmt = fmt
         self.a = arrays
+        self.hot_mode = hot_mode
         hid = arrays.get("hot_ids", np.zeros(0, np.int32))
         self.hot = {int(e): s for s, e in enumerate(np.asarray(hid).tolist())}
 
     def is_fp8(self, e: int) -> bool:
-        return e in self.hot
+        return e in self.hot and self.hot_mode == "replace"
 
     def fp8_image(self, e: int, which: int):
         """The converted FP8 workspace image of hot expert e's W{which}."""
         s = self.hot[e]
         return F.mxfp4_to_fp8(self.a[f"hot_w{which}_codes"][s], self.a[f"hot_w{which}_scales"][s])
 
-    def dense(self, e: int, which: int) -> np.ndarray:
-        if e in self.hot:
-            return F.dequant_fp8(*self.fp8_image(e, which))
+    def low_bit(self, e: int, which: int) -> np.ndarray:
+        """The low-bit weights of expert e's W{which}, decoded."""
         c, s = self.a[f"w{which}_codes"][e], self.a[f"w{which}_scales"][e]
         return F.dequant_w2(c, s) if self.fmt == "w2" else F.dequant_w3(c, s)
+
+    def residual(self, e: int, which: int) -> np.ndarray:
+        """The MXFP4 residual of hot expert e's W{which} (residual mode), decoded."""
+        s = self.hot[e]
+        return F.dequant_mxfp4(self.a[f"hot_w{which}_codes"][s], self.a[f"hot_w{which}_scales"][s])
+
+    def dense(self, e: int, which: int) -> np.ndarray:
+        if e in self.hot:
+            if self.hot_mode == "replace":
+                return F.dequant_fp8(*self.fp8_image(e, which))
+            return self.low_bit(e, which) + self.residual(e, which)
+        return self.low_bit(e, which)
 
 
 def expert_ffn(layer: Layer, x_bits, k: int, offsets, perm, experts=None):

@@ -2,6 +2,7 @@
 inputs, closed forms, special cases that reduce to a dense MLP, and the expert-sum
 identity.  None of these re-types the oracle's own formula."""
 import math
+import os
 
 import numpy as np
 import pytest
@@ -232,3 +233,118 @@ def test_expert_subset_rows():
     lo, hi = full["offsets"][1], full["offsets"][2]
     np.testing.assert_array_equal(part[lo:hi], full["y_perm"][lo:hi])
     assert np.all(np.isnan(part[:lo])) and np.all(np.isnan(part[hi:]))
+
+
+# ------------------------------------------------------------- FP4 residual (delta cache)
+RES_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "residual.txt")
+
+
+def _res_golden():
+    out = []
+    for line in open(RES_GOLDEN):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        lhs, rhs = line.split("->")
+        words, scale, byte, e8 = lhs.split()
+        out.append(([int(w, 16) for w in words.split(",")], int(scale, 16), int(byte, 16), int(e8),
+                    [float(v) for v in rhs.split(",")]))
+    return out
+
+
+def _residual_layer(E=4, H=64, I=32, hot=2, seed=0):
+    sp = moegen.spec("tiny", E=E, H=H, I=I, n_hot=hot, index=95 + seed, hot_mode="residual")
+    return sp, M.Layer("w2", moegen.weights(sp), hot_mode="residual")
+
+
+@pytest.mark.parametrize("words,scale,byte,e8,vals", _res_golden())
+def test_residual_hand_worked_rows(words, scale, byte, e8, vals):
+    """One hot-expert row (32 weights): 2-bit weights plus the MXFP4 residual, against the
+    hand-derived values in tests/golden/residual.txt."""
+    a = {"w1_codes": np.array(words, np.uint32).reshape(1, 1, 2), "w1_scales": np.array([[[scale]]], np.uint16),
+         "w2_codes": np.zeros((1, 1, 2), np.uint32), "w2_scales": np.zeros((1, 1, 1), np.uint16),
+         "hot_ids": np.array([0], np.int32),
+         "hot_w1_codes": np.full((1, 1, 16), byte, np.uint8), "hot_w1_scales": np.array([[[e8]]], np.uint8),
+         "hot_w2_codes": np.zeros((1, 1, 16), np.uint8), "hot_w2_scales": np.zeros((1, 1, 1), np.uint8)}
+    lay = M.Layer("w2", a, hot_mode="residual")
+    np.testing.assert_array_equal(lay.dense(0, 1)[0] * 2.0**7, np.array(vals))
+
+
+def test_residual_zero_delta_is_the_2bit_layer():
+    """All residual nibbles zero (any scale): the layer is the 2-bit layer, bit for bit."""
+    sp, lay = _residual_layer(E=6, hot=3)
+    a0 = dict(lay.a)
+    for key in ("hot_w1_codes", "hot_w2_codes"):
+        a0[key] = np.zeros_like(a0[key])
+    zero = M.Layer("w2", a0, hot_mode="residual")
+    plain = M.Layer("w2", {k_: v for k_, v in lay.a.items() if not k_.startswith("hot_")})
+    b = moegen.batch(sp, 11)
+    r0 = M.layer_forward(zero, b["logits"], b["x"], 2)
+    r1 = M.layer_forward(plain, b["logits"], b["x"], 2)
+    np.testing.assert_array_equal(r0["out"], r1["out"])
+    assert any(int(e) in set(r0["ids"].reshape(-1).tolist()) for e in lay.a["hot_ids"])
+
+
+def test_residual_zero_2bit_scales_give_the_mxfp4_weights():
+    sp, lay = _residual_layer()
+    a0 = dict(lay.a)
+    for key in ("w1_scales", "w2_scales"):
+        a0[key] = np.zeros_like(a0[key])
+    z = M.Layer("w2", a0, hot_mode="residual")
+    for s, e in enumerate(lay.a["hot_ids"]):
+        for which in (1, 2):
+            want = F.dequant_mxfp4(lay.a[f"hot_w{which}_codes"][s], lay.a[f"hot_w{which}_scales"][s])
+            np.testing.assert_array_equal(z.dense(int(e), which), want)
+
+
+def _bits_w2(words, scales, K):
+    """2-bit weights by Python bit loops (not the oracle's unpacking)."""
+    rows = words.shape[0]
+    out = np.zeros((rows, K))
+    for r in range(rows):
+        for k in range(K):
+            c = (int(words[r, k // 16]) >> (2 * (k % 16))) & 3
+            s = np.array([int(scales[r, k // 32]) << 16], np.uint32).view(np.float32)[0]
+            out[r, k] = (-4.0, -1.0, 1.0, 4.0)[c] * float(s)
+    return out
+
+
+def _bits_mxfp4(codes, scales, K):
+    """MXFP4 weights by Python bit loops."""
+    mag = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+    rows = codes.shape[0]
+    out = np.zeros((rows, K))
+    for r in range(rows):
+        for k in range(K):
+            n = (int(codes[r, k // 2]) >> (4 * (k % 2))) & 15
+            v = mag[n & 7] * (-1.0 if n & 8 else 1.0)
+            out[r, k] = v * 2.0 ** (int(scales[r, k // 32]) - 127)
+    return out
+
+
+def test_residual_single_expert_layer_is_a_dense_mlp_torch():
+    """E = 1, k = 1, the expert hot: the layer is one SwiGLU MLP on W = W_2bit + W_mxfp4, with
+    both parts unpacked here by bit loops and the MLP evaluated by torch (float64)."""
+    sp, lay = _residual_layer(E=1, hot=1, H=64, I=32)
+    b = moegen.batch(sp, 7)
+    res = M.layer_forward(lay, b["logits"][:, :1], b["x"], 1)
+    a = lay.a
+    W1 = _bits_w2(a["w1_codes"][0], a["w1_scales"][0], 64) + _bits_mxfp4(a["hot_w1_codes"][0], a["hot_w1_scales"][0], 64)
+    W2 = _bits_w2(a["w2_codes"][0], a["w2_scales"][0], 32) + _bits_mxfp4(a["hot_w2_codes"][0], a["hot_w2_scales"][0], 32)
+    X = torch.from_numpy(F.bf16_value(b["x"]))
+    h = torch.nn.functional.linear(X, torch.from_numpy(W1))
+    h = torch.nn.functional.silu(h[:, :32]) * h[:, 32:]
+    y = torch.nn.functional.linear(h, torch.from_numpy(W2)).numpy()
+    np.testing.assert_allclose(res["out"], y, rtol=1e-12, atol=1e-12 * np.abs(y).max())
+    # the residual matters: without it the output moves
+    plain = M.Layer("w2", {k_: v for k_, v in a.items() if not k_.startswith("hot_")})
+    r0 = M.layer_forward(plain, b["logits"][:, :1], b["x"], 1)
+    assert np.max(np.abs(r0["out"] - res["out"])) > 1e-3 * np.abs(y).max()
+
+
+def test_residual_experts_compute_without_fp8_activations():
+    sp, lay = _residual_layer()
+    e = int(lay.a["hot_ids"][0])
+    assert not lay.is_fp8(e) and e in lay.hot
+    rep = M.Layer("w2", lay.a, hot_mode="replace")
+    assert rep.is_fp8(e)
