@@ -51,6 +51,7 @@ _SIGS = {
     "moe_expert_ffn_ws_bytes": (_sz, [ctypes.POINTER(MoeWeights), _i32, _i32, _i32]),
     "moe_expert_ffn": (_i32, [ctypes.POINTER(MoeWeights), _p, _i32, _i32, _p, _p, _p, _p, _p, _sz, _p]),
     "moe_expert_ffn_num_stages": (_i32, [ctypes.POINTER(MoeWeights), _i32, _i32, _sz]),
+    "moe_expert_ffn_noalloc": (_i32, [ctypes.POINTER(MoeWeights), _p, _i32, _i32, _p, _p, _p, _p, _p]),
     "moe_expert_ffn_stage": (_i32, [ctypes.POINTER(MoeWeights), _p, _i32, _i32, _p, _p, _p, _p, _p, _sz, _i32,
                                     _p]),
     "moe_combine": (_i32, [_p, _p, _p, _i32, _i32, _i32, _p, _i32, _p]),
@@ -174,6 +175,19 @@ def moe_expert_ffn(w: DeviceWeights, x: torch.Tensor, k: int, counts, offsets, p
         ws = torch.empty(max(1, moe_expert_ffn_ws_bytes(w, T, k, slots)), dtype=torch.uint8, device=x.device)
     _check("moe_expert_ffn", lib.moe_expert_ffn(ctypes.byref(w.c), _ptr(x), T, k, _ptr(counts), _ptr(offsets),
                                                 _ptr(perm), _ptr(y_perm), _ptr(ws), ws.numel(), _stream()))
+    return y_perm
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # MOE_NOALLOC_SCRATCH_BYTES
+
+
+def moe_expert_ffn_noalloc(w: DeviceWeights, x: torch.Tensor, k: int, counts, offsets, perm, y_perm):
+    """moe_expert_ffn with the library's static workspace (no allocation by the library; y_perm is
+    the caller's)."""
+    _dev(x, torch.int16, "x (bf16 bits as int16)")
+    T = x.shape[0]
+    _check("moe_expert_ffn_noalloc", lib.moe_expert_ffn_noalloc(ctypes.byref(w.c), _ptr(x), T, k, _ptr(counts),
+                                                                _ptr(offsets), _ptr(perm), _ptr(y_perm), _stream()))
     return y_perm
 
 

@@ -2,6 +2,8 @@
 // workspace layout and kernel dispatch.  No allocation, no host synchronisation.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "../../include/bitmoe.h"
 #include "kernels.h"
 
@@ -300,6 +302,56 @@ int32_t moe_expert_ffn_num_stages(const moe_weights* w, int32_t T, int32_t k, si
   if (check_weights(w) != MOE_OK || T < 0 || k < 1) return 0;
   if (T == 0) return 0;
   return ffn_num_stages(w, T, k, ws_bytes);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ the allocation-free variant
+// A workspace that lives in the library: one copy per GPU, held until the process ends.  The
+// host-side name `scratch` is not a device address; its address on each device comes from
+// hipGetSymbolAddress, taken once per device with that device current, and only that address is
+// passed to the kernels.
+namespace {
+
+constexpr size_t kStaticScratchBytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of this device's scratch array (nullptr on failure).
+void* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_expert_ffn_noalloc(const moe_weights* w, const uint16_t* x, int32_t T, int32_t k,
+                                  const int32_t* counts, const int32_t* offsets, const int32_t* perm,
+                                  float* y_perm, void* stream) {
+  moe_status st = check_weights(w);
+  if (st != MOE_OK) return st;
+  if (T < 0 || k < 1 || k > w->E || (int64_t)T * k >= ((int64_t)1 << 31)) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  // the batch must fit the static workspace (with at least one FP8 slot for a hot set)
+  const FfnLayout L = ffn_layout(w, T, k);
+  if (L.fixed > kStaticScratchBytes || (w->n_hot > 0 && ffn_slots(w, L, kStaticScratchBytes) < 1))
+    return MOE_ERR_WORKSPACE;
+  void* ws = device_scratch();
+  if (!ws) return MOE_ERR_HIP;
+  return moe_expert_ffn(w, x, T, k, counts, offsets, perm, y_perm, ws, kStaticScratchBytes, stream);
 }
 
 moe_status moe_expert_ffn_stage(const moe_weights* w, const uint16_t* x, int32_t T, int32_t k,

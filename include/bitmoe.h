@@ -159,6 +159,22 @@ moe_status moe_expert_ffn(const moe_weights* w, const uint16_t* x, int32_t T, in
                           const int32_t* counts, const int32_t* offsets, const int32_t* perm,
                           float* y_perm, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_expert_ffn_noalloc -- moe_expert_ffn with its workspace inside the library, for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving loops, harnesses that
+ * forbid allocation).  It allocates nothing: the workspace is a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES bytes, one per GPU the library runs on, held until the process ends;
+ * its device address is looked up once per device, on that device's first call.  Same kernels,
+ * same results as moe_expert_ffn with a caller workspace of that size (with a hot set, as many
+ * FP8 slots as fit, at least one).  Every call on one GPU uses that GPU's array: calls that
+ * overlap on one GPU (other streams, other threads) race and must be serialised by the caller.
+ * Errors: as moe_expert_ffn; WORKSPACE if the batch needs more than the static workspace
+ * (moe_expert_ffn_ws_bytes(w, T, k, 1) > MOE_NOALLOC_SCRATCH_BYTES); HIP if the array's device
+ * address cannot be obtained. */
+#define MOE_NOALLOC_SCRATCH_BYTES (16u << 20)
+moe_status moe_expert_ffn_noalloc(const moe_weights* w, const uint16_t* x, int32_t T, int32_t k,
+                                  const int32_t* counts, const int32_t* offsets, const int32_t* perm,
+                                  float* y_perm, void* stream);
+
 /* moe_expert_ffn_stage -- run one stage of moe_expert_ffn.  Calling stages 0 .. n-1, with
  * n = moe_expert_ffn_num_stages(w, T, k, ws_bytes), in order on one stream with the same
  * arguments and workspace is exactly moe_expert_ffn.  Each stage is a single kernel launch, so
