@@ -142,7 +142,8 @@ def setup_layer(name: str):
     print(f"[bench] generating layer {name} (E={sp['E']} k={sp['k']} H={sp['H']} I={sp['I']} {sp['fmt']})",
           file=sys.stderr, flush=True)
     arrays = moegen.weights(sp)
-    dw = L.DeviceWeights({"w2": 1, "w3": 2}[sp["fmt"]], sp["E"], sp["H"], sp["I"], arrays)
+    flags = L.MOE_FLAG_HOT_RESIDUAL if sp["hot_mode"] == "residual" else 0
+    dw = L.DeviceWeights({"w2": 1, "w3": 2}[sp["fmt"]], sp["E"], sp["H"], sp["I"], arrays, flags=flags)
     return sp, dw
 
 
@@ -265,12 +266,16 @@ def measure(sp: dict, dw, T: int, steps: int, warmup: int, flush_between: bool =
     n_hot_active = int(((counts > 0) & hot).sum().item())
     n_cold_active = n_active - n_hot_active
     hot_rows = int(counts[hot].sum().item())
-    w1b = n_cold_active * weight_bytes_per_expert(sp, 1) + n_hot_active * weight_bytes_per_expert(sp, 1, "mxfp4")
-    w2b = n_cold_active * weight_bytes_per_expert(sp, 2) + n_hot_active * weight_bytes_per_expert(sp, 2, "mxfp4")
+    residual = sp["hot_mode"] == "residual"  # hot experts: 2-bit codes + an MXFP4 residual, both read
+    hot_b = {which: weight_bytes_per_expert(sp, which, "mxfp4") + (weight_bytes_per_expert(sp, which) if residual else 0)
+             for which in (1, 2)}
+    w1b = n_cold_active * weight_bytes_per_expert(sp, 1) + n_hot_active * hot_b[1]
+    w2b = n_cold_active * weight_bytes_per_expert(sp, 2) + n_hot_active * hot_b[2]
     gemm = T >= GEMM_MIN_TOKENS and not batch_invariant  # the invariant mode streams every group
     workload = f"{sp['name']} MoE layer E={E} top-{k} H={H} I={I} {sp['fmt']} T={T}"
     if sp["n_hot"] > 0:
-        workload += f" ({sp['n_hot']} hot experts mxfp4->fp8)"
+        workload += (f" ({sp['n_hot']} hot experts with an mxfp4 residual)" if residual
+                     else f" ({sp['n_hot']} hot experts mxfp4->fp8)")
     if batch_invariant:
         workload += " batch-invariant mode"
     if hot_batches > 0 and hot_rows > 0:
@@ -298,7 +303,8 @@ def measure(sp: dict, dw, T: int, steps: int, warmup: int, flush_between: bool =
         fc1_bytes = w1b + T * H * 2 + R * I * 2
         roof_ms = float(np.mean(stage_ms[1]))  # the streaming kernel (stage 2 launches nothing)
         achieved = fc1_bytes / (roof_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": "moe_expert_ffn stage 1: FC1 + SwiGLU weight streaming (stream_kernel<W2Fmt, 1, G>)",
+        roof = {"bound": "hbm", "kernel": "moe_expert_ffn stage 1: FC1 + SwiGLU weight streaming (stream_kernel<"
+                + ("W3Fmt" if sp["fmt"] == "w3" else "W2Fmt") + ", 1, G, " + ("true" if residual else "false") + ">)",
                 "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "alg_bytes_per_launch": fc1_bytes}
     roof["traffic"] = measured_traffic(workload)
@@ -307,7 +313,7 @@ def measure(sp: dict, dw, T: int, steps: int, warmup: int, flush_between: bool =
     # the whole layer against its roofline: t_roof = max(flops_bf16 / P_bf16 + flops_fp8 / P_fp8,
     # algorithmic bytes / HBM peak), with the bytes = packed weights of the experts that received
     # rows + logits + x + out (bf16)
-    f_fp8 = 2.0 * hot_rows * 3 * I * H
+    f_fp8 = 0.0 if residual else 2.0 * hot_rows * 3 * I * H
     f_bf16 = all_flops - f_fp8
     t_mfma = (f_bf16 / (BF16_PEAK_TFLOPS * 1e12) + f_fp8 / (FP8_PEAK_TFLOPS * 1e12)) * 1e3
     layer_bytes = w1b + w2b + T * E * 4 + T * H * 2 + T * H * 2
@@ -504,7 +510,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--layer", default="decode", help="decode | prefill | mixed | w3 | tiny | quantize (the quantisers, not a layer)")
+    ap.add_argument("--layer", default="decode",
+                    help="decode | prefill | mixed | residual | w3 | tiny | quantize (the quantisers, not a layer)")
     ap.add_argument("--T", type=int, default=64)
     ap.add_argument("--no-flush", action="store_true", help="do not flush caches between steps")
     ap.add_argument("--tier-slots", type=int, default=0,

@@ -37,6 +37,7 @@ class MoeWeights(ctypes.Structure):
 
 
 MOE_FLAG_BATCH_INVARIANT = 1
+MOE_FLAG_HOT_RESIDUAL = 2
 
 
 class MoeTierState(ctypes.Structure):
@@ -314,8 +315,8 @@ def moe_fp8_slot_layout(H: int, I: int) -> dict:
 
 def moe_debug_dequant(w: DeviceWeights, e: int, which: int):
     """which: 1 / 2 = W1 / W2 through the streaming kernels' decoder, 3 / 4 through the grouped
-    GEMM's decoder."""
-    rows, K = (2 * w.I, w.H) if which in (1, 3) else (w.H, w.I)
+    GEMM's decoder, 5 / 6 the FP4 residual of hot slot e (layers with MOE_FLAG_HOT_RESIDUAL)."""
+    rows, K = (2 * w.I, w.H) if which in (1, 3, 5) else (w.H, w.I)
     out = torch.empty((rows, K), dtype=torch.float32, device="cuda")
     _check("moe_debug_dequant", lib.moe_debug_dequant(ctypes.byref(w.c), e, which, _ptr(out), _stream()))
     return out

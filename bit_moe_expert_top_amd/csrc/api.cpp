@@ -35,6 +35,11 @@ constexpr int kGemmMinTokens = 128;
 // formed in the same order for every T: the split fixes how K is cut and summed, and the kernels
 // treat each token column of a tile on its own, so the item size (16 or 32 rows) does not matter.
 inline bool invariant(const moe_weights* w) { return (w->flags & MOE_FLAG_BATCH_INVARIANT) != 0; }
+// A hot set held as an FP4 residual on top of the experts' 2-bit codes: no FP8 path, the hot
+// experts stream with a second (residual) pass.
+inline bool hot_residual(const moe_weights* w) { return (w->flags & MOE_FLAG_HOT_RESIDUAL) != 0 && w->n_hot > 0; }
+// A hot set computed on the FP8 path (MXFP4 held, converted into workspace slots).
+inline bool hot_fp8(const moe_weights* w) { return w->n_hot > 0 && !hot_residual(w); }
 inline int stream_chunk(int T) { return T <= 16 ? 16 : kStreamChunk; }
 inline int split_tokens(const moe_weights* w, int T) { return invariant(w) ? 16 : T; }
 
@@ -72,7 +77,7 @@ FfnLayout ffn_layout(const moe_weights* w, int T, int k) {
   L.hot_max_items = 0;
   L.hot_plan_off = L.xq_off = L.xqs_off = L.hq_off = L.hqs_off = L.slots_off = off;
   L.slot_bytes = 0;
-  if (w->n_hot > 0) {
+  if (hot_fp8(w)) {
     L.hot_max_items = (R + kHotChunk - 1) / kHotChunk + (R < w->n_hot ? R : w->n_hot);
     L.hot_plan_off = off;
     off = align256(off + plan_bytes(L.hot_max_items));
@@ -93,7 +98,7 @@ FfnLayout ffn_layout(const moe_weights* w, int T, int k) {
 
 // FP8 slots that fit in ws_bytes (capped at n_hot); 0 if none fits or there is no hot set.
 int ffn_slots(const moe_weights* w, const FfnLayout& L, size_t ws_bytes) {
-  if (w->n_hot <= 0 || ws_bytes < L.fixed) return 0;
+  if (!hot_fp8(w) || ws_bytes < L.fixed) return 0;
   const size_t s = (ws_bytes - L.fixed) / L.slot_bytes;
   return (int)(s < (size_t)w->n_hot ? s : (size_t)w->n_hot);
 }
@@ -109,10 +114,12 @@ moe_status check_weights(const moe_weights* w) {
   if (w->H % 256 || w->I % 256 || w->H > 16384 || w->I > 16384) return MOE_ERR_UNSUPPORTED;
   if (!w->w1_codes || !w->w1_scales || !w->w2_codes || !w->w2_scales) return MOE_ERR_INVALID_ARG;
   if (w->n_hot < 0 || w->n_hot > w->E) return MOE_ERR_INVALID_ARG;
-  if (w->flags & ~MOE_FLAG_BATCH_INVARIANT) return MOE_ERR_INVALID_ARG;
+  if (w->flags & ~(MOE_FLAG_BATCH_INVARIANT | MOE_FLAG_HOT_RESIDUAL)) return MOE_ERR_INVALID_ARG;
   if (w->n_hot > 0 && (!w->hot_ids || !w->hot_w1_codes || !w->hot_w1_scales || !w->hot_w2_codes ||
                        !w->hot_w2_scales))
     return MOE_ERR_INVALID_ARG;
+  // the FP4 residual sits on 2-bit experts
+  if (hot_residual(w) && w->fmt != MOE_FMT_W2) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -135,6 +142,12 @@ LowbitWeights lowbit(const moe_weights* w) {
   l.w1_scales = w->w1_scales;
   l.w2_codes = w->w2_codes;
   l.w2_scales = w->w2_scales;
+  if (hot_residual(w)) {
+    l.res_w1_codes = w->hot_w1_codes;
+    l.res_w1_scales = w->hot_w1_scales;
+    l.res_w2_codes = w->hot_w2_codes;
+    l.res_w2_scales = w->hot_w2_scales;
+  }
   return l;
 }
 
@@ -189,7 +202,7 @@ moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
 size_t moe_expert_ffn_ws_bytes(const moe_weights* w, int32_t T, int32_t k, int32_t fp8_slots) {
   if (check_weights(w) != MOE_OK || T <= 0 || k <= 0) return 0;
   const FfnLayout L = ffn_layout(w, T, k);
-  if (w->n_hot == 0) return L.fixed;
+  if (!hot_fp8(w)) return L.fixed;
   const int s = (fp8_slots <= 0 || fp8_slots > w->n_hot) ? w->n_hot : fp8_slots;
   return L.fixed + (size_t)s * L.slot_bytes;
 }
@@ -210,7 +223,7 @@ moe_status ffn_check(const moe_weights* w, const uint16_t* x, int32_t T, int32_t
   if ((int64_t)T * w->H * 2 >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
   const FfnLayout L = ffn_layout(w, T, k);
   if (!ws || ws_bytes < L.fixed) return MOE_ERR_WORKSPACE;
-  if (w->n_hot > 0 && ffn_slots(w, L, ws_bytes) < 1) return MOE_ERR_WORKSPACE;
+  if (hot_fp8(w) && ffn_slots(w, L, ws_bytes) < 1) return MOE_ERR_WORKSPACE;
   return MOE_OK;
 }
 
@@ -222,7 +235,7 @@ moe_status ffn_check(const moe_weights* w, const uint16_t* x, int32_t T, int32_t
 constexpr int kLowbitStages = 5;
 
 int ffn_num_stages(const moe_weights* w, int T, int k, size_t ws_bytes) {
-  if (w->n_hot <= 0) return kLowbitStages;
+  if (!hot_fp8(w)) return kLowbitStages;
   const int S = ffn_slots(w, ffn_layout(w, T, k), ws_bytes);
   if (S < 1) return kLowbitStages + 1;
   return kLowbitStages + 1 + 3 * ((w->n_hot + S - 1) / S);
@@ -241,8 +254,8 @@ moe_status ffn_run_stage(const moe_weights* w, const uint16_t* x, int32_t T, int
   hipError_t e = hipSuccess;
   switch (stage) {
     case 0:
-      e = launch_prepare(offsets, w->E, stream_chunk(T), kGemmRows, L.gemm, w->hot_ids, w->n_hot, plan_s, plan_g,
-                         x, T, w->H, lw.fmt, xp, s);
+      e = launch_prepare(offsets, w->E, stream_chunk(T), kGemmRows, L.gemm, w->hot_ids, w->n_hot, hot_residual(w),
+                         plan_s, plan_g, x, T, w->H, lw.fmt, xp, s);
       break;
     case 1:
       e = launch_lowbit_fc1(lw, w->E, w->H, w->I, k, xp, perm, plan_s, (int)L.max_items_s, T,
@@ -347,7 +360,7 @@ moe_status moe_expert_ffn_noalloc(const moe_weights* w, const uint16_t* x, int32
   if (T == 0) return MOE_OK;
   // the batch must fit the static workspace (with at least one FP8 slot for a hot set)
   const FfnLayout L = ffn_layout(w, T, k);
-  if (L.fixed > kStaticScratchBytes || (w->n_hot > 0 && ffn_slots(w, L, kStaticScratchBytes) < 1))
+  if (L.fixed > kStaticScratchBytes || (hot_fp8(w) && ffn_slots(w, L, kStaticScratchBytes) < 1))
     return MOE_ERR_WORKSPACE;
   void* ws = device_scratch();
   if (!ws) return MOE_ERR_HIP;
@@ -410,7 +423,12 @@ moe_status moe_debug_dequant(const moe_weights* w, int32_t e, int32_t which, flo
                              void* stream) {
   moe_status st = check_weights(w);
   if (st != MOE_OK) return st;
-  if (e < 0 || e >= w->E || which < 1 || which > 4 || !out) return MOE_ERR_INVALID_ARG;
+  if (e < 0 || e >= w->E || which < 1 || which > 6 || !out) return MOE_ERR_INVALID_ARG;
+  if (which >= 5) {  // the FP4 residual of hot slot e
+    if (!hot_residual(w)) return MOE_ERR_UNSUPPORTED;
+    if (e >= w->n_hot) return MOE_ERR_INVALID_ARG;
+    return from_hip(launch_debug_dequant_residual(lowbit(w), w->H, w->I, e, which - 4, out, as_stream(stream)));
+  }
   if (which <= 2)
     return from_hip(launch_debug_dequant(lowbit(w), w->E, w->H, w->I, e, which, out, as_stream(stream)));
   return from_hip(launch_debug_dequant_gemm(lowbit(w), w->H, w->I, e, which - 2, out, as_stream(stream)));
@@ -423,7 +441,7 @@ moe_status moe_expert_ffn_ws_region(const moe_weights* w, int32_t T, int32_t k, 
   if (T < 1 || k < 1 || k > w->E || (int64_t)T * k >= ((int64_t)1 << 31) || !offset || !bytes)
     return MOE_ERR_INVALID_ARG;
   if (region < MOE_WS_XQ || region > MOE_WS_SLOTS) return MOE_ERR_INVALID_ARG;
-  if (w->n_hot <= 0) return MOE_ERR_UNSUPPORTED;
+  if (!hot_fp8(w)) return MOE_ERR_UNSUPPORTED;
   const FfnLayout L = ffn_layout(w, T, k);
   const int S = ffn_slots(w, L, ws_bytes);
   if (S < 1) return MOE_ERR_WORKSPACE;

@@ -32,7 +32,7 @@ size_t plan_bytes(int64_t max_items) { return (size_t)(16 + 16 * max_items); }
 __global__ __launch_bounds__(1024) void prepare_kernel(const int32_t* __restrict__ offsets, int E,
                                                        int small_max, int gemm_chunk, int gemm_enabled,
                                                        const int32_t* __restrict__ hot_ids, int n_hot,
-                                                       int32_t* __restrict__ plan_s,
+                                                       int hot_residual, int32_t* __restrict__ plan_s,
                                                        int32_t* __restrict__ plan_g,
                                                        const uint4* __restrict__ x, int nchunks,
                                                        int fmt, uint4* __restrict__ xp) {
@@ -75,17 +75,19 @@ __global__ __launch_bounds__(1024) void prepare_kernel(const int32_t* __restrict
     }
     return;
   }
-  build_plan2(offsets, E, small_max, gemm_chunk, gemm_enabled, hot_ids, n_hot, plan_s, plan_g);
+  build_plan2(offsets, E, small_max, gemm_chunk, gemm_enabled, hot_ids, n_hot, hot_residual, plan_s, plan_g);
 }
 
 hipError_t launch_prepare(const int32_t* offsets, int E, int small_max, int gemm_chunk, bool gemm_enabled,
-                          const int32_t* hot_ids, int n_hot, int32_t* plan_s, int32_t* plan_g,
-                          const uint16_t* x, int T, int H, int fmt, uint16_t* xp, hipStream_t s) {
+                          const int32_t* hot_ids, int n_hot, bool hot_residual, int32_t* plan_s,
+                          int32_t* plan_g, const uint16_t* x, int T, int H, int fmt, uint16_t* xp,
+                          hipStream_t s) {
   const int per = fmt == W2Fmt::kId ? 16 : 32;  // k per thread
   const int nchunks = xp ? T * (H / per) : 0;
   const int blocks = 1 + (nchunks + 1023) / 1024;
   prepare_kernel<<<blocks, 1024, 0, s>>>(offsets, E, small_max, gemm_chunk, gemm_enabled ? 1 : 0, hot_ids,
-                                         n_hot, plan_s, plan_g, (const uint4*)x, nchunks, fmt, (uint4*)xp);
+                                         n_hot, hot_residual ? 1 : 0, plan_s, plan_g, (const uint4*)x, nchunks,
+                                         fmt, (uint4*)xp);
   return hipGetLastError();
 }
 
@@ -110,32 +112,51 @@ constexpr int kRT = 4;  // 16-row A tiles per wave (64 weight rows)
 constexpr int kBStage = 4 * 16 * 512;  // the largest stage: KS = 4 x 16 tokens (or KS = 1 x 32)
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Per-wave pipeline state: the codes of two super-steps (the current one and the next, issued
-// one super-step ahead), the scales of the current and the next super-step, the accumulators.
+// Per-wave pipeline state of one pass over K: the weight resources and this lane's offsets, the
+// codes of two super-steps (the current one and the next, issued one super-step ahead), the
+// scales of the current and the next super-step.  The accumulators live outside, so that a
+// second pass (the FP4 residual of a hot expert) adds into the same sums.
 template <class F, int NT, int G>
 struct Pipe {
   static constexpr int SB = F::kStepScaleBytes * G;
+  buf_rsrc rc, rs;
+  uint32_t coff[kRT], soff[kRT];
   typename F::Codes cw[2][G][kRT];
   ScaleBytes<SB> sc[kRT], sc_next[kRT];
-  f32x4 acc[kRT][NT];
 };
 
 // Codes of super-step c (all G steps, issued together) into ring slot `slot`.
 template <class F, int NT, int G>
-__device__ __forceinline__ void load_codes(Pipe<F, NT, G>& P, int slot, buf_rsrc rc,
-                                           const uint32_t* coff, int c) {
+__device__ __forceinline__ void load_codes(Pipe<F, NT, G>& P, int slot, int c) {
 #pragma unroll
   for (int t = 0; t < kRT; ++t)
 #pragma unroll
     for (int s = 0; s < G; ++s)
-      P.cw[slot][s][t] = F::load_codes(rc, coff[t] + F::code_bytes(256u * G * (uint32_t)c + 64u * (uint32_t)s));
+      P.cw[slot][s][t] = F::load_codes(P.rc, P.coff[t] + F::code_bytes(256u * G * (uint32_t)c + 64u * (uint32_t)s));
 }
 
 template <class F, int NT, int G>
-__device__ __forceinline__ void load_scales(Pipe<F, NT, G>& P, buf_rsrc rs, const uint32_t* soff, int c) {
+__device__ __forceinline__ void load_scales(Pipe<F, NT, G>& P, int c) {
 #pragma unroll
   for (int t = 0; t < kRT; ++t)
-    P.sc_next[t] = load_scale_bytes<Pipe<F, NT, G>::SB>(rs, soff[t] + F::scale_bytes(256u * G * (uint32_t)c));
+    P.sc_next[t] = load_scale_bytes<Pipe<F, NT, G>::SB>(P.rs, P.soff[t] + F::scale_bytes(256u * G * (uint32_t)c));
+}
+
+// The weight resources of one expert (or one hot slot of the residual arrays) and this lane's
+// code and scale offsets: tile t of the wave is weight row row[t] + (lane % 16); the lane's
+// k range starts at kq.
+template <class F, int NT, int G>
+__device__ __forceinline__ void pipe_init(Pipe<F, NT, G>& P, const uint8_t* __restrict__ codes,
+                                          const uint8_t* __restrict__ scales, size_t ebase, int rows_per_expert,
+                                          int K, const int* row, int kq) {
+  const uint32_t cbr = F::code_bytes((uint32_t)K), sbr = F::scale_bytes((uint32_t)K);
+  P.rc = make_rsrc(codes + ebase * cbr, (uint32_t)rows_per_expert * cbr);
+  P.rs = make_rsrc(scales + ebase * sbr, (uint32_t)rows_per_expert * sbr);
+#pragma unroll
+  for (int t = 0; t < kRT; ++t) {
+    P.coff[t] = (uint32_t)row[t] * cbr + F::code_bytes((uint32_t)kq);
+    P.soff[t] = (uint32_t)row[t] * sbr + F::scale_bytes((uint32_t)kq);
+  }
 }
 
 // Direct loads of the token operand of step st into a stage buffer: round u of this wave
@@ -166,12 +187,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 //      the next super-step's codes and scales (issued after B(st)) may stay in flight -- then
 //      a barrier: B(st) of every wave is in LDS and every wave is done with B(st-1);
 //   2. issue B(st+1) into the other stage; at S = 0 then issue the codes and scales of
-//      super-step c+1; decode + MFMA.
+//      super-step c+1; decode + MFMA, the token operands read one operand ahead of their
+//      MFMAs (the LDS latency hides behind the decode).
 template <class F, int NT, int G, int CS, int BS, int S>
-__device__ __forceinline__ void step(Pipe<F, NT, G>& P, buf_rsrc rc, buf_rsrc rs, buf_rsrc rb, uint8_t* bs0,
-                                     uint8_t* bs1, const uint32_t* coff, const uint32_t* soff,
-                                     const uint32_t* doff, uint32_t active, int wu, const uint32_t* bread,
-                                     int c, int n_it) {
+__device__ __forceinline__ void step(Pipe<F, NT, G>& P, f32x4 (&acc)[kRT][NT], buf_rsrc rb, uint8_t* bs0,
+                                     uint8_t* bs1, const uint32_t* doff, uint32_t active, int wu,
+                                     const uint32_t* bread, int c, int n_it) {
   constexpr int kLc = F::kStepCodeBytes > 16 ? 2 : 1;  // load instructions per tile and step
   constexpr int kAfter = S == 1 ? kRT * (1 + G * kLc) : 0;
   const int st = G * c + S;
@@ -182,24 +203,30 @@ __device__ __forceinline__ void step(Pipe<F, NT, G>& P, buf_rsrc rc, buf_rsrc rs
     const int n_ss = n_it / G;
 #pragma unroll
     for (int t = 0; t < kRT; ++t) P.sc[t] = P.sc_next[t];
-    load_scales<F, NT, G>(P, rs, soff, min(c + 1, n_ss - 1));
-    load_codes<F, NT, G>(P, CS ^ 1, rc, coff, min(c + 1, n_ss - 1));
+    load_scales<F, NT, G>(P, min(c + 1, n_ss - 1));
+    load_codes<F, NT, G>(P, CS ^ 1, min(c + 1, n_ss - 1));
   }
   __builtin_amdgcn_sched_barrier(0);
   const uint8_t* bsrc = BS ? bs1 : bs0;
   typename F::Tab tab[kRT];
 #pragma unroll
   for (int t = 0; t < kRT; ++t) tab[t] = F::table(F::step_scale(P.sc[t], S));
+  u32x4 b[2][NT];
+#pragma unroll
+  for (int bt = 0; bt < NT; ++bt) b[0][bt] = *reinterpret_cast<const u32x4*>(bsrc + bread[bt * 8]);
 #pragma unroll
   for (int o = 0; o < 8; ++o) {
-    u32x4 b[NT];
+    if (o + 1 < 8) {
 #pragma unroll
-    for (int bt = 0; bt < NT; ++bt) b[bt] = *reinterpret_cast<const u32x4*>(bsrc + bread[bt * 8 + o]);
+      for (int bt = 0; bt < NT; ++bt)
+        b[(o + 1) & 1][bt] = *reinterpret_cast<const u32x4*>(bsrc + bread[bt * 8 + o + 1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the next operand's reads ahead of this decode
 #pragma unroll
     for (int t = 0; t < kRT; ++t) {
       const u32x4 a = F::decode(P.cw[CS][S][t], tab[t], o);
 #pragma unroll
-      for (int bt = 0; bt < NT; ++bt) P.acc[t][bt] = mfma_16x16x32_bf16(a, b[bt], P.acc[t][bt]);
+      for (int bt = 0; bt < NT; ++bt) acc[t][bt] = mfma_16x16x32_bf16(a, b[o & 1][bt], acc[t][bt]);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -207,72 +234,36 @@ __device__ __forceinline__ void step(Pipe<F, NT, G>& P, buf_rsrc rc, buf_rsrc rs
 
 // One super-step c (code ring slot CS = c % 2).
 template <class F, int NT, int G, int CS>
-__device__ __forceinline__ void superstep(Pipe<F, NT, G>& P, buf_rsrc rc, buf_rsrc rs, buf_rsrc rb,
-                                          uint8_t* bs0, uint8_t* bs1, const uint32_t* coff,
-                                          const uint32_t* soff, const uint32_t* doff, uint32_t active,
-                                          int wu, const uint32_t* bread, int c, int n_it) {
+__device__ __forceinline__ void superstep(Pipe<F, NT, G>& P, f32x4 (&acc)[kRT][NT], buf_rsrc rb, uint8_t* bs0,
+                                          uint8_t* bs1, const uint32_t* doff, uint32_t active, int wu,
+                                          const uint32_t* bread, int c, int n_it) {
   // B stage of step G*c + S is its parity: S for G = 2, CS for G = 1
-  step<F, NT, G, CS, (G == 1 ? CS : 0), 0>(P, rc, rs, rb, bs0, bs1, coff, soff, doff, active, wu, bread, c, n_it);
-  if constexpr (G == 2)
-    step<F, NT, G, CS, 1, 1>(P, rc, rs, rb, bs0, bs1, coff, soff, doff, active, wu, bread, c, n_it);
+  step<F, NT, G, CS, (G == 1 ? CS : 0), 0>(P, acc, rb, bs0, bs1, doff, active, wu, bread, c, n_it);
+  if constexpr (G == 2) step<F, NT, G, CS, 1, 1>(P, acc, rb, bs0, bs1, doff, active, wu, bread, c, n_it);
 }
 
-// One wave's task: 64 weight rows (4 A tiles) x a K range, for the NT*16 tokens of one item.
-//   FC == 1: tiles 0,1 = gate rows 32rb + [0,32), tiles 2,3 = up rows I + 32rb + [0,32) of W1;
-//            epilogue h[r][32rb + pos32(c)] = silu(gate) * up for c in [0,32), stored bf16.
-//   FC == 2: tiles t = rows 64rb + 16t + [0,16) of W2; epilogue y[r][64rb + 16t + f] (fp32).
-// The 4 waves of a workgroup take 4/KS row blocks x KS parts of K; K parts are summed in LDS.
-template <class F, int FC, int NT, int G>
-__device__ __forceinline__ void stream_task(const uint8_t* __restrict__ codes,
-                                            const uint8_t* __restrict__ scales, size_t ebase,
-                                            int rows_per_expert, int K, int width, int ktop,
-                                            const uint16_t* __restrict__ bsrc, uint32_t bsrc_bytes,
-                                            const int32_t* __restrict__ perm, int blk_rb, int KS,
-                                            int r0, int nrows, void* __restrict__ out, uint8_t* bs0,
-                                            uint8_t* bs1) {
-  const int lane = wave_lane(), w = threadIdx.x / kWave;
-  const int wu = __builtin_amdgcn_readfirstlane(w);
-  const int i16 = lane & 15, q = lane >> 4;
-  const int kpart = w % KS, rb_i = blk_rb * (4 / KS) + w / KS;
-  const int n_it = (K / 256) / KS;      // steps of this wave (a multiple of G)
-  const int k0 = 256 * n_it * kpart;    // first k of this wave
-  const uint32_t cbr = F::code_bytes((uint32_t)K), sbr = F::scale_bytes((uint32_t)K);
-  // per-expert buffers (uniform base, byte size) and per-lane byte offsets
-  const buf_rsrc rc = make_rsrc(codes + ebase * cbr, (uint32_t)rows_per_expert * cbr);
-  const buf_rsrc rs = make_rsrc(scales + ebase * sbr, (uint32_t)rows_per_expert * sbr);
-  // FC1 gathers token rows of x (all of x is addressable, < 4 GiB); FC2 reads the item's own h
-  // rows, so its resource is based at row r0 (h may exceed 4 GiB)
-  const buf_rsrc rb = FC == 1 ? make_rsrc(bsrc, bsrc_bytes)
-                              : make_rsrc(bsrc + (size_t)r0 * K, (uint32_t)nrows * (uint32_t)K * 2u);
-  // Source row of each of the item's (<= 32) tokens: lane i looks up token i once (one
-  // branch-free load, issued before the prologue's code loads so the two latencies overlap),
-  // and the B rounds below read it from that lane.
-  uint32_t lane_row = (uint32_t)min(lane & 31, nrows - 1);
-  uint32_t perm_v = 0;
-  if constexpr (FC == 1) perm_v = (uint32_t)perm[r0 + (int)lane_row];
-  uint32_t coff[kRT], soff[kRT];
-#pragma unroll
-  for (int t = 0; t < kRT; ++t) {
-    const int row = FC == 1 ? (t < 2 ? 32 * rb_i + 16 * t : width + 32 * rb_i + 16 * (t - 2)) + i16
-                            : 64 * rb_i + 16 * t + i16;
-    coff[t] = (uint32_t)row * cbr + F::code_bytes((uint32_t)(k0 + 64 * G * q));
-    soff[t] = (uint32_t)row * sbr + F::scale_bytes((uint32_t)(k0 + 64 * G * q));
+// The super-steps of one pass (the prologue's loads of super-step 0 and of B(0) issued).
+template <class F, int NT, int G>
+__device__ __forceinline__ void stream_loop(Pipe<F, NT, G>& P, f32x4 (&acc)[kRT][NT], buf_rsrc rb, uint8_t* bs0,
+                                            uint8_t* bs1, const uint32_t* doff, uint32_t active, int wu,
+                                            const uint32_t* bread, int n_it) {
+  const int n_ss = n_it / G;
+  int c = 0;
+  for (; c + 1 < n_ss; c += 2) {
+    superstep<F, NT, G, 0>(P, acc, rb, bs0, bs1, doff, active, wu, bread, c, n_it);
+    superstep<F, NT, G, 1>(P, acc, rb, bs0, bs1, doff, active, wu, bread, c + 1, n_it);
   }
-  Pipe<F, NT, G> P;
-#pragma unroll
-  for (int t = 0; t < kRT; ++t)
-#pragma unroll
-    for (int bt = 0; bt < NT; ++bt) P.acc[t][bt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // prologue: scales and codes of super-step 0 (B of step 0 below, once its rows are known)
-  load_scales<F, NT, G>(P, rs, soff, 0);
-  load_codes<F, NT, G>(P, 0, rc, coff, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  if constexpr (FC == 1) lane_row = perm_v / (uint32_t)ktop;
-  // B stage: KS parts x 16*NT tokens x 32 chunks of 16 bytes; chunk c of token n sits at
-  // position c ^ (n & 7) of the token's 512 bytes.
-  const int per_part = NT * 16 * 32;    // chunks per K part
-  const int nrounds = KS * NT * 2;      // 256-chunk rounds of the workgroup (<= 8)
-  uint32_t doff[8];
+  if (c < n_ss) superstep<F, NT, G, 0>(P, acc, rb, bs0, bs1, doff, active, wu, bread, c, n_it);
+}
+
+// Source offsets of this lane's direct B loads (one per 256-chunk round u of the workgroup) for
+// super-steps of G steps: chunk c of token n of K part p (position c ^ (n & 7) in the token's
+// 512 bytes of the stage) holds the 8 k at 64*G*(c/8) + 8*(c%8) of the part's current step.
+// Rounds past the item's rows get kOffNone (they load zeros).
+template <int NT, int G>
+__device__ __forceinline__ void b_offsets(uint32_t* doff, int w, int lane, int nrows, int K, int n_it, int nrounds,
+                                          uint32_t lane_row) {
+  const int per_part = NT * 16 * 32;  // chunks per K part
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int f = 256 * u + 64 * w + lane;
@@ -284,6 +275,64 @@ __device__ __forceinline__ void stream_task(const uint8_t* __restrict__ codes,
                        16u * (uint32_t)(c & 7);
     doff[u] = (u < nrounds && n < nrows) ? o : kOffNone;
   }
+}
+
+// One wave's task: 64 weight rows (4 A tiles) x a K range, for the NT*16 tokens of one item.
+//   FC == 1: tiles 0,1 = gate rows 32rb + [0,32), tiles 2,3 = up rows I + 32rb + [0,32) of W1;
+//            epilogue h[r][32rb + pos32(c)] = silu(gate) * up for c in [0,32), stored bf16.
+//   FC == 2: tiles t = rows 64rb + 16t + [0,16) of W2; epilogue y[r][64rb + 16t + f] (fp32).
+// The 4 waves of a workgroup take 4/KS row blocks x KS parts of K; K parts are summed in LDS.
+// RES: a hot expert of a layer with an FP4 residual (rslot >= 0) makes a second pass over the
+// same rows and k with the residual's MXFP4 codes, into the same accumulators.
+template <class F, int FC, int NT, int G, bool RES>
+__device__ __forceinline__ void stream_task(const uint8_t* __restrict__ codes,
+                                            const uint8_t* __restrict__ scales, size_t ebase,
+                                            int rows_per_expert, int K, int width, int ktop,
+                                            const uint16_t* __restrict__ bsrc, uint32_t bsrc_bytes,
+                                            const int32_t* __restrict__ perm, int blk_rb, int KS,
+                                            int r0, int nrows, void* __restrict__ out, uint8_t* bs0,
+                                            uint8_t* bs1, const uint8_t* __restrict__ rcodes,
+                                            const uint8_t* __restrict__ rscales, int rslot) {
+  const int lane = wave_lane(), w = threadIdx.x / kWave;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int i16 = lane & 15, q = lane >> 4;
+  const int kpart = w % KS, rb_i = blk_rb * (4 / KS) + w / KS;
+  const int n_it = (K / 256) / KS;      // steps of this wave (a multiple of G)
+  const int k0 = 256 * n_it * kpart;    // first k of this wave
+  // FC1 gathers token rows of x (all of x is addressable, < 4 GiB); FC2 reads the item's own h
+  // rows, so its resource is based at row r0 (h may exceed 4 GiB)
+  const buf_rsrc rb = FC == 1 ? make_rsrc(bsrc, bsrc_bytes)
+                              : make_rsrc(bsrc + (size_t)r0 * K, (uint32_t)nrows * (uint32_t)K * 2u);
+  // Source row of each of the item's (<= 32) tokens: lane i looks up token i once (one
+  // branch-free load, issued before the prologue's code loads so the two latencies overlap),
+  // and the B rounds below read it from that lane.
+  uint32_t lane_row = (uint32_t)min(lane & 31, nrows - 1);
+  uint32_t perm_v = 0;
+  if constexpr (FC == 1) perm_v = (uint32_t)perm[r0 + (int)lane_row];
+  int row[kRT];
+#pragma unroll
+  for (int t = 0; t < kRT; ++t)
+    row[t] = FC == 1 ? (t < 2 ? 32 * rb_i + 16 * t : width + 32 * rb_i + 16 * (t - 2)) + i16
+                     : 64 * rb_i + 16 * t + i16;
+  const int kq = k0 + 64 * G * q;
+  Pipe<F, NT, G> P;
+  pipe_init<F, NT, G>(P, codes, scales, ebase, rows_per_expert, K, row, kq);
+  f32x4 acc[kRT][NT];
+#pragma unroll
+  for (int t = 0; t < kRT; ++t)
+#pragma unroll
+    for (int bt = 0; bt < NT; ++bt) acc[t][bt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // prologue: scales and codes of super-step 0 (B of step 0 below, once its rows are known)
+  load_scales<F, NT, G>(P, 0);
+  load_codes<F, NT, G>(P, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (FC == 1) lane_row = perm_v / (uint32_t)ktop;
+  // B stage: KS parts x 16*NT tokens x 32 chunks of 16 bytes; chunk c of token n sits at
+  // position c ^ (n & 7) of the token's 512 bytes.
+  const int per_part = NT * 16 * 32;    // chunks per K part
+  const int nrounds = KS * NT * 2;      // 256-chunk rounds of the workgroup (<= 8)
+  uint32_t doff[8];
+  b_offsets<NT, G>(doff, w, lane, nrows, K, n_it, nrounds, lane_row);
   // rounds of this wave that carry at least one real token row (a round of a wave covers the
   // 2 token rows of its 64 chunks); the others are not issued
   uint32_t active = 0;
@@ -301,13 +350,25 @@ __device__ __forceinline__ void stream_task(const uint8_t* __restrict__ codes,
 
   dma_b<G>(rb, bs0, doff, active, wu, 0);
   __builtin_amdgcn_sched_barrier(0);
-  const int n_ss = n_it / G;
-  int c = 0;
-  for (; c + 1 < n_ss; c += 2) {
-    superstep<F, NT, G, 0>(P, rc, rs, rb, bs0, bs1, coff, soff, doff, active, wu, bread, c, n_it);
-    superstep<F, NT, G, 1>(P, rc, rs, rb, bs0, bs1, coff, soff, doff, active, wu, bread, c + 1, n_it);
+  stream_loop<F, NT, G>(P, acc, rb, bs0, bs1, doff, active, wu, bread, n_it);
+  if constexpr (RES) {
+    if (rslot >= 0) {  // uniform over the workgroup (one item)
+      // the residual pass: 32 code bytes per lane and step, so super-steps of one step (a
+      // two-step code ring would not fit the registers), with the B offsets of that k mapping
+      constexpr int GR = 1;
+      __syncthreads();  // every wave is done reading the B stages of the first pass
+      Pipe<Fp4Fmt, NT, GR> R;
+      pipe_init<Fp4Fmt, NT, GR>(R, rcodes, rscales, (size_t)rslot * rows_per_expert, rows_per_expert, K, row,
+                                k0 + 64 * GR * q);
+      load_scales<Fp4Fmt, NT, GR>(R, 0);
+      load_codes<Fp4Fmt, NT, GR>(R, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      b_offsets<NT, GR>(doff, w, lane, nrows, K, n_it, nrounds, lane_row);
+      dma_b<GR>(rb, bs0, doff, active, wu, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      stream_loop<Fp4Fmt, NT, GR>(R, acc, rb, bs0, bs1, doff, active, wu, bread, n_it);
+    }
   }
-  if (c < n_ss) superstep<F, NT, G, 0>(P, rc, rs, rb, bs0, bs1, coff, soff, doff, active, wu, bread, c, n_it);
 
   // Epilogue, one token tile at a time.  With KS > 1 the K parts of the waves that share a
   // row block are summed through LDS (over the first B stage, free now) in a fixed order.
@@ -318,7 +379,7 @@ __device__ __forceinline__ void stream_task(const uint8_t* __restrict__ codes,
     f32x4 v[kRT];
     if (KS > 1) {
 #pragma unroll
-      for (int t = 0; t < kRT; ++t) red[w][t][lane] = P.acc[t][bt];
+      for (int t = 0; t < kRT; ++t) red[w][t][lane] = acc[t][bt];
       __syncthreads();
       const int w0 = w - kpart;  // first wave of this row block
 #pragma unroll
@@ -329,7 +390,7 @@ __device__ __forceinline__ void stream_task(const uint8_t* __restrict__ codes,
       }
     } else {
 #pragma unroll
-      for (int t = 0; t < kRT; ++t) v[t] = P.acc[t][bt];
+      for (int t = 0; t < kRT; ++t) v[t] = acc[t][bt];
     }
     const int n = 16 * bt + i16;
     if (kpart == 0 && n < nrows) {
@@ -355,12 +416,13 @@ __device__ __forceinline__ void stream_task(const uint8_t* __restrict__ codes,
 }
 
 // Tasks (item, row-block group) in a grid-stride loop; an item (<= 32 rows) uses one or two
-// 16-token tiles.
-template <class F, int FC, int G>
+// 16-token tiles.  With RES, an item whose hot slot (item.w) is >= 0 adds the FP4 residual.
+template <class F, int FC, int G, bool RES>
 __global__ __launch_bounds__(256, 2) void stream_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int rows_per_expert,
     int K, int width, int ktop, const uint16_t* __restrict__ bsrc, const int32_t* __restrict__ perm,
-    const int32_t* __restrict__ plan, uint32_t bsrc_bytes, int KS, void* __restrict__ out) {
+    const int32_t* __restrict__ plan, uint32_t bsrc_bytes, int KS, void* __restrict__ out,
+    const uint8_t* __restrict__ rcodes, const uint8_t* __restrict__ rscales) {
   __shared__ __align__(16) uint8_t bs0[kBStage];
   __shared__ __align__(16) uint8_t bs1[kBStage];
   const int n_items = plan[0];
@@ -373,12 +435,13 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(
     const int4 itm = items[item];
     const size_t ebase = (size_t)itm.x * rows_per_expert;
     const int r0 = itm.y, nrows = itm.z;
+    const int rslot = RES ? itm.w : -1;
     if (nrows <= 16)
-      stream_task<F, FC, 1, G>(codes, scales, ebase, rows_per_expert, K, width, ktop, bsrc, bsrc_bytes,
-                               perm, grp, KS, r0, nrows, out, bs0, bs1);
+      stream_task<F, FC, 1, G, RES>(codes, scales, ebase, rows_per_expert, K, width, ktop, bsrc, bsrc_bytes,
+                                    perm, grp, KS, r0, nrows, out, bs0, bs1, rcodes, rscales, rslot);
     else
-      stream_task<F, FC, 2, G>(codes, scales, ebase, rows_per_expert, K, width, ktop, bsrc, bsrc_bytes,
-                               perm, grp, KS, r0, nrows, out, bs0, bs1);
+      stream_task<F, FC, 2, G, RES>(codes, scales, ebase, rows_per_expert, K, width, ktop, bsrc, bsrc_bytes,
+                                    perm, grp, KS, r0, nrows, out, bs0, bs1, rcodes, rscales, rslot);
   }
 }
 
@@ -405,18 +468,22 @@ static int super_step_for(int K, int ks) {
   return n % 2 == 0 ? 2 : 1;
 }
 
-template <class F, int FC>
+template <class F, int FC, bool RES>
 static hipError_t launch_stream(const void* codes, const void* scales, int rows, int K, int width,
                                 int ktop, const uint16_t* bsrc, const int32_t* perm,
                                 const int32_t* plan, uint32_t bsrc_bytes, int ks, int64_t tasks,
-                                hipStream_t s, void* out) {
+                                hipStream_t s, void* out, const void* rcodes, const void* rscales) {
   const int g = super_step_for(K, ks), grid = grid_for(tasks);
   const uint8_t* c = (const uint8_t*)codes;
   const uint8_t* sc = (const uint8_t*)scales;
+  const uint8_t* rc = (const uint8_t*)rcodes;
+  const uint8_t* rs = (const uint8_t*)rscales;
   if (g == 2)
-    stream_kernel<F, FC, 2><<<grid, 256, 0, s>>>(c, sc, rows, K, width, ktop, bsrc, perm, plan, bsrc_bytes, ks, out);
+    stream_kernel<F, FC, 2, RES><<<grid, 256, 0, s>>>(c, sc, rows, K, width, ktop, bsrc, perm, plan, bsrc_bytes, ks,
+                                                      out, rc, rs);
   else
-    stream_kernel<F, FC, 1><<<grid, 256, 0, s>>>(c, sc, rows, K, width, ktop, bsrc, perm, plan, bsrc_bytes, ks, out);
+    stream_kernel<F, FC, 1, RES><<<grid, 256, 0, s>>>(c, sc, rows, K, width, ktop, bsrc, perm, plan, bsrc_bytes, ks,
+                                                      out, rc, rs);
   return hipGetLastError();
 }
 
@@ -427,10 +494,15 @@ hipError_t launch_lowbit_fc1(const LowbitWeights& w, int E, int H, int I, int k,
   const int ks = k_split_for(split_T, H, w.fmt);
   const int64_t tasks = (int64_t)max_items * ((I / 32) / (4 / ks));
   const uint32_t xb = (uint32_t)((size_t)T * H * 2);
+  if (w.fmt == W2Fmt::kId && w.res_w1_codes)
+    return launch_stream<W2Fmt, 1, true>(w.w1_codes, w.w1_scales, 2 * I, H, I, k, xp, perm, plan, xb, ks, tasks, s,
+                                         hbuf, w.res_w1_codes, w.res_w1_scales);
   if (w.fmt == W2Fmt::kId)
-    return launch_stream<W2Fmt, 1>(w.w1_codes, w.w1_scales, 2 * I, H, I, k, xp, perm, plan, xb, ks, tasks, s, hbuf);
+    return launch_stream<W2Fmt, 1, false>(w.w1_codes, w.w1_scales, 2 * I, H, I, k, xp, perm, plan, xb, ks, tasks, s,
+                                          hbuf, nullptr, nullptr);
   if (w.fmt == W3Fmt::kId)
-    return launch_stream<W3Fmt, 1>(w.w1_codes, w.w1_scales, 2 * I, H, I, k, xp, perm, plan, xb, ks, tasks, s, hbuf);
+    return launch_stream<W3Fmt, 1, false>(w.w1_codes, w.w1_scales, 2 * I, H, I, k, xp, perm, plan, xb, ks, tasks, s,
+                                          hbuf, nullptr, nullptr);
   return hipErrorInvalidValue;
 }
 
@@ -442,10 +514,15 @@ hipError_t launch_lowbit_fc2(const LowbitWeights& w, int E, int H, int I, int k,
   const int ks = k_split_for(split_T, I, w.fmt);
   const int64_t tasks = (int64_t)max_items * ((H / 64) / (4 / ks));
   const uint32_t hb = 0;  // unused: FC2 bases its resource at each item's rows
+  if (w.fmt == W2Fmt::kId && w.res_w2_codes)
+    return launch_stream<W2Fmt, 2, true>(w.w2_codes, w.w2_scales, H, I, H, 1, hbuf, nullptr, plan, hb, ks, tasks, s,
+                                         y, w.res_w2_codes, w.res_w2_scales);
   if (w.fmt == W2Fmt::kId)
-    return launch_stream<W2Fmt, 2>(w.w2_codes, w.w2_scales, H, I, H, 1, hbuf, nullptr, plan, hb, ks, tasks, s, y);
+    return launch_stream<W2Fmt, 2, false>(w.w2_codes, w.w2_scales, H, I, H, 1, hbuf, nullptr, plan, hb, ks, tasks, s,
+                                          y, nullptr, nullptr);
   if (w.fmt == W3Fmt::kId)
-    return launch_stream<W3Fmt, 2>(w.w2_codes, w.w2_scales, H, I, H, 1, hbuf, nullptr, plan, hb, ks, tasks, s, y);
+    return launch_stream<W3Fmt, 2, false>(w.w2_codes, w.w2_scales, H, I, H, 1, hbuf, nullptr, plan, hb, ks, tasks, s,
+                                          y, nullptr, nullptr);
   return hipErrorInvalidValue;
 }
 
@@ -500,6 +577,20 @@ hipError_t launch_debug_dequant(const LowbitWeights& w, int E, int H, int I, int
   } else {
     return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_dequant_residual(const LowbitWeights& w, int H, int I, int slot, int which, float* out,
+                                         hipStream_t s) {
+  const int rows = which == 1 ? 2 * I : H;
+  const int K = which == 1 ? H : I;
+  const uint8_t* codes = (const uint8_t*)(which == 1 ? w.res_w1_codes : w.res_w2_codes);
+  const uint8_t* scales = (const uint8_t*)(which == 1 ? w.res_w1_scales : w.res_w2_scales);
+  if (!codes || !scales) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)rows * (K / 64);
+  const unsigned grid = (unsigned)((n + 255) / 256);
+  const size_t cb = (size_t)slot * rows * Fp4Fmt::code_bytes(K), sb = (size_t)slot * rows * Fp4Fmt::scale_bytes(K);
+  debug_dequant_kernel<Fp4Fmt><<<grid, 256, 0, s>>>(codes + cb, scales + sb, rows, K, out);
   return hipGetLastError();
 }
 

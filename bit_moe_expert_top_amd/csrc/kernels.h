@@ -30,6 +30,12 @@ struct LowbitWeights {
   const void* w1_scales;
   const void* w2_codes;
   const void* w2_scales;
+  // FP4 residual of the hot experts (2-bit layers with a residual hot set; else null):
+  // MXFP4 arrays stacked along the hot slots, W1 [n_hot][2I][H/2], W2 [n_hot][H][I/2]
+  const void* res_w1_codes = nullptr;
+  const void* res_w1_scales = nullptr;
+  const void* res_w2_codes = nullptr;
+  const void* res_w2_scales = nullptr;
 };
 
 // Work list of grouped-row chunks built on the device from `offsets`.
@@ -37,10 +43,13 @@ struct LowbitWeights {
 size_t plan_bytes(int64_t max_items);
 // One launch: the two low-bit work lists (streaming items of <= small_max rows; grouped-GEMM
 // items of <= gemm_chunk rows for experts above small_max if gemm_enabled), and (if xp) x
-// stored in the k-slot order of the weight format `fmt` (1 = 2-bit, 2 = 3-bit).
+// stored in the k-slot order of the weight format `fmt` (1 = 2-bit, 2 = 3-bit).  Hot experts
+// are left out (they run on the FP8 path), unless hot_residual: then they join the streaming
+// list whatever their size, their items carrying their hot slot.
 hipError_t launch_prepare(const int32_t* offsets, int E, int small_max, int gemm_chunk, bool gemm_enabled,
-                          const int32_t* hot_ids, int n_hot, int32_t* plan_s, int32_t* plan_g,
-                          const uint16_t* x, int T, int H, int fmt, uint16_t* xp, hipStream_t s);
+                          const int32_t* hot_ids, int n_hot, bool hot_residual, int32_t* plan_s,
+                          int32_t* plan_g, const uint16_t* x, int T, int H, int fmt, uint16_t* xp,
+                          hipStream_t s);
 
 // Decode-style kernels: weight-streaming, MFMA on 16-token tiles.
 // split_T: the batch size the K split across a workgroup's waves is chosen for (T itself, or 1
@@ -104,6 +113,9 @@ hipError_t launch_hot_fc2(int H, int I, int64_t R, const int32_t* hot_plan, int 
 
 hipError_t launch_debug_dequant(const LowbitWeights& w, int E, int H, int I, int e, int which,
                                 float* out, hipStream_t s);
+// The FP4 residual of hot slot `slot` through the streaming kernels' residual decoder.
+hipError_t launch_debug_dequant_residual(const LowbitWeights& w, int H, int I, int slot, int which, float* out,
+                                         hipStream_t s);
 // The same through the grouped GEMM's field decoder (F::table32 / F::decode32).
 hipError_t launch_debug_dequant_gemm(const LowbitWeights& w, int H, int I, int e, int which, float* out,
                                      hipStream_t s);

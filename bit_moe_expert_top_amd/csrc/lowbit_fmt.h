@@ -247,4 +247,84 @@ struct W3Fmt {
   }
 };
 
+// =====================================================================================
+// MXFP4 residual of a 2-bit expert ([Moet-QA]: the FP4 delta cache above the 2-bit weights;
+// [OCP-MX] e2m1 elements, one e8m0 scale per 32 along K): codes u8[rows][K/2] (element 2i in
+// the low nibble), scales u8[rows][K/32].  Decoded to exact bf16 values e2m1 * 2^(scale - 127)
+// in the 2-bit format's k-slot order, so that its MFMAs share the token operand of the 2-bit
+// pass and accumulate into the same sums (the residual is added before SwiGLU).
+//
+// Per 32-k group a lane builds byte tables of the eight magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}
+// times the scale (high and low bytes, 2 x 2 dwords: the bf16 bits of each magnitude plus
+// (scale - 127) << 7, one packed 16-bit add per pair; magnitude 0 stays 0).  The bytes of a
+// 16-k block holding the slot's k (even bytes for slots 0-7 -- k 0,4,8,12 in the low nibbles,
+// k 1,5,9,13 in the high ones -- odd bytes for slots 8-15) are gathered by one v_perm_b32; the
+// magnitudes masked into selector bytes are looked up in both tables, the nibble's sign bit is
+// xor-ed into the high byte, and two v_perm_b32 interleave high and low bytes into bf16 pairs.
+// Exact for scale bytes in [2, 252] (every nonzero value then a normal bf16).
+// =====================================================================================
+struct Fp4Fmt {
+  static constexpr int kId = 3;
+  static constexpr int kStepCodeBytes = 32;  // 64 codes
+  static constexpr int kStepScaleBytes = 2;  // 2 e8m0 bytes
+  __host__ __device__ static constexpr uint32_t code_bytes(uint32_t k) { return k / 2; }
+  __host__ __device__ static constexpr uint32_t scale_bytes(uint32_t k) { return k / 32; }
+
+  struct Codes { u32x4 a, b; };
+  struct GTab { uint32_t hb0, hb1, lb0, lb1; };  // magnitudes 0-3 / 4-7, high / low bytes
+  struct Tab { GTab g[2]; };                      // the step's two groups
+
+  __device__ static __forceinline__ Codes load_codes(buf_rsrc r, uint32_t off) {
+    return {buf_load16(r, off), buf_load16(r, off + 16u)};
+  }
+  __device__ static __forceinline__ GTab group_table(uint32_t e) {
+    // bf16 bits of the magnitudes at scale 1, in pairs; + (e - 127) << 7 on every nonzero one
+    const uint16_t x = (uint16_t)((e - 127u) << 7);
+    const u16x2 p0 = u16x2{0, 0x3F00} + u16x2{0, x};
+    const u16x2 p1 = u16x2{0x3F80, 0x3FC0} + u16x2{x, x};
+    const u16x2 p2 = u16x2{0x4000, 0x4040} + u16x2{x, x};
+    const u16x2 p3 = u16x2{0x4080, 0x40C0} + u16x2{x, x};
+    const uint32_t d0 = __builtin_bit_cast(uint32_t, p0), d1 = __builtin_bit_cast(uint32_t, p1);
+    const uint32_t d2 = __builtin_bit_cast(uint32_t, p2), d3 = __builtin_bit_cast(uint32_t, p3);
+    GTab t;
+    t.hb0 = byte_perm(d1, d0, 0x07050301u);
+    t.lb0 = byte_perm(d1, d0, 0x06040200u);
+    t.hb1 = byte_perm(d3, d2, 0x07050301u);
+    t.lb1 = byte_perm(d3, d2, 0x06040200u);
+    return t;
+  }
+  // the step's scale bytes: group 0 in bits [0, 8), group 1 in bits [8, 16)
+  __device__ static __forceinline__ Tab table(uint32_t sw) {
+    Tab t;
+    t.g[0] = group_table(sw & 0xFFu);
+    t.g[1] = group_table((sw >> 8) & 0xFFu);
+    return t;
+  }
+  template <int NB>
+  __device__ static __forceinline__ uint32_t step_scale(const ScaleBytes<NB>& s, int step) {
+    return (s.v[step >> 1] >> (16 * (step & 1))) & 0xFFFFu;
+  }
+  // four magnitudes (selector bytes) with their signs (bit 7 of each byte) -> two bf16 pairs
+  __device__ static __forceinline__ void lookup(uint32_t m, uint32_t sg, const GTab& t, uint32_t& d0,
+                                                uint32_t& d1) {
+    const uint32_t hb = byte_perm(t.hb1, t.hb0, m) ^ sg, lb = byte_perm(t.lb1, t.lb0, m);
+    d0 = byte_perm(hb, lb, 0x05010400u);
+    d1 = byte_perm(hb, lb, 0x07030602u);
+  }
+  // operand o (0..7) of a step: 16-k block o / 2 (code dwords 2(o/2), 2(o/2)+1), slots 8(o%2) ..
+  __device__ static __forceinline__ u32x4 decode(const Codes& c, const Tab& t, int o) {
+    const int j = o >> 1;
+    const uint32_t d_lo = j < 2 ? c.a[2 * j] : c.b[2 * j - 4];
+    const uint32_t d_hi = j < 2 ? c.a[2 * j + 1] : c.b[2 * j - 3];
+    const uint32_t g = byte_perm(d_hi, d_lo, (o & 1) ? 0x07050301u : 0x06040200u);
+    const GTab& tb = t.g[j >> 1];
+    uint32_t d0, d1, d2, d3;
+    lookup(g & 0x07070707u, (g << 4) & 0x80808080u, tb, d0, d1);   // low nibbles
+    lookup((g >> 4) & 0x07070707u, g & 0x80808080u, tb, d2, d3);  // high nibbles
+    return u32x4{d0, d1, d2, d3};
+  }
+  __host__ __device__ static constexpr int pos32(int c) { return W2Fmt::pos32(c); }
+  __host__ __device__ static constexpr int slot_k(int s) { return W2Fmt::slot_k(s); }
+};
+
 }  // namespace bitmoe

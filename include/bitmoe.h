@@ -90,7 +90,8 @@ typedef struct {
   const void* hot_w1_scales;   /* [n_hot][2I][H/32] u8 e8m0                                  */
   const void* hot_w2_codes;    /* [n_hot][H][I/2]   u8                                       */
   const void* hot_w2_scales;   /* [n_hot][H][I/32]  u8 e8m0                                  */
-  int32_t flags;               /* 0 or MOE_FLAG_BATCH_INVARIANT; other bits: INVALID_ARG     */
+  int32_t flags;               /* MOE_FLAG_BATCH_INVARIANT | MOE_FLAG_HOT_RESIDUAL; others:
+                                  INVALID_ARG                                                */
 } moe_weights;
 
 /* [Moet-README] (results table of the DeepSeek-V4.1-Flash build, quality row): a request gives
@@ -103,6 +104,21 @@ typedef struct {
  * stay within the same tolerance of the exact result).  Routing, grouping, the FP8 hot path
  * and the combine compute each token on its own in both modes. */
 #define MOE_FLAG_BATCH_INVARIANT 1
+
+/* [Moet-QA] (the FP4 delta cache: the hottest experts keep an FP4-precision correction layer
+ * above their 2-bit weights) and [Moet-README] (README line "2-bit experts on vLLM v0.24.0": a
+ * 2-bit codebook plus an FP4 delta cache).
+ * With this flag the hot set is a residual, not a replacement: a hot expert keeps its 2-bit
+ * codes and scales in the low-bit arrays (they are read), and its MXFP4 arrays (hot_w1_codes ..,
+ * stacked along [n_hot] in the order of hot_ids) hold a correction added to those weights,
+ * element by element, before the matmuls: W = level * scale + e2m1 * 2^(e8m0 - 127).  The sum is
+ * computed with bf16 operands and fp32 accumulation like the 2-bit experts (the FFN kernels make
+ * a second pass over the residual into the same sums, so it is added before SwiGLU); there is
+ * no FP8 path and no FP8 workspace.  Hot experts then run on the weight-streaming kernels at
+ * any batch size.  Requires fmt == MOE_FMT_W2 (else UNSUPPORTED); residual scale bytes must lie
+ * in [2, 252] (every decoded value then a normal bf16).  Without a hot set the flag has no
+ * effect. */
+#define MOE_FLAG_HOT_RESIDUAL 2
 
 /* moe_route -- top-k routing ([Moet-README]: each token is served by k routed experts).
  *   logits    f32[T][E]   router logits
@@ -331,7 +347,9 @@ moe_status moe_tier_remap(const int32_t* topk_ids, int64_t R, const int32_t* slo
  * kernels use, into f32[rows][K] (W1: rows = 2I, K = H; W2: rows = H, K = I), in natural K
  * order.  For tests: the decoded weights must equal the format definition bit for bit.
  *   which: 1 (W1) or 2 (W2) through the weight-streaming kernels' decoder; 3 (W1) or 4 (W2)
- *          through the grouped-GEMM kernels' decoder (one 32-k field per lane).
+ *          through the grouped-GEMM kernels' decoder (one 32-k field per lane); 5 (W1) or 6
+ *          (W2): the FP4 residual of hot slot e (MOE_FLAG_HOT_RESIDUAL layers only, else
+ *          UNSUPPORTED) through the streaming kernels' residual decoder.
  * Errors: INVALID_ARG, UNSUPPORTED. */
 moe_status moe_debug_dequant(const moe_weights* w, int32_t e, int32_t which, float* out,
                              void* stream);

@@ -25,12 +25,13 @@ def device_layer(name: str, **override):
     from bit_moe_expert_top_amd import _lib as L
 
     sp, arrays = layer_arrays(name, **override)
-    return sp, L.DeviceWeights(FMT[sp["fmt"]], sp["E"], sp["H"], sp["I"], arrays)
+    flags = L.MOE_FLAG_HOT_RESIDUAL if sp["hot_mode"] == "residual" else 0
+    return sp, L.DeviceWeights(FMT[sp["fmt"]], sp["E"], sp["H"], sp["I"], arrays, flags=flags)
 
 
 def oracle_layer(name: str, **override):
     sp, arrays = layer_arrays(name, **override)
-    return OM.Layer(sp["fmt"], arrays)
+    return OM.Layer(sp["fmt"], arrays, hot_mode=sp["hot_mode"])
 
 
 def to_dev(a: np.ndarray) -> torch.Tensor:

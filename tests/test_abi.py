@@ -100,7 +100,7 @@ def test_ffn_flags(lib):
 
     p = 16
     base = (8, 256, 512, L.MOE_FMT_W2, p, p, p, p, 0, None, None, None, None, None)
-    unknown = L.MoeWeights(*base, 2)
+    unknown = L.MoeWeights(*base, 4)
     assert L.lib.moe_expert_ffn_ws_bytes(ctypes.byref(unknown), 256, 2, 0) == 0
     assert L.lib.moe_expert_ffn(ctypes.byref(unknown), p, 16, 2, p, p, p, p, p, 1 << 30, None) == -1
     plain = L.MoeWeights(*base, 0)
@@ -114,6 +114,19 @@ def test_ffn_flags(lib):
     assert L.lib.moe_expert_ffn_num_stages(ctypes.byref(inv), 256, 2, 1 << 30) == 5
     dw = L.MoeWeights(*base)
     assert dw.flags == 0
+    # FP4 residual hot set: no FP8 stages; only on 2-bit experts
+    hot = (8, 256, 512, L.MOE_FMT_W2, p, p, p, p, 2, p, p, p, p, p)
+    res = L.MoeWeights(*hot, L.MOE_FLAG_HOT_RESIDUAL)
+    fp8 = L.MoeWeights(*hot, 0)
+    assert L.lib.moe_expert_ffn_num_stages(ctypes.byref(res), 256, 2, 1 << 30) == 5
+    assert L.lib.moe_expert_ffn_num_stages(ctypes.byref(fp8), 256, 2, 1 << 30) > 5
+    assert L.lib.moe_expert_ffn_ws_bytes(ctypes.byref(res), 256, 2, 0) < L.lib.moe_expert_ffn_ws_bytes(
+        ctypes.byref(fp8), 256, 2, 0)
+    w3res = L.MoeWeights(8, 256, 512, L.MOE_FMT_W3, p, p, p, p, 2, p, p, p, p, p, L.MOE_FLAG_HOT_RESIDUAL)
+    assert L.lib.moe_expert_ffn(ctypes.byref(w3res), p, 16, 2, p, p, p, p, p, 1 << 30, None) == -2
+    off, n = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert L.lib.moe_expert_ffn_ws_region(ctypes.byref(res), 16, 2, 1 << 30, L.MOE_WS_HQ, ctypes.byref(off),
+                                          ctypes.byref(n)) == -2
     header = open(os.path.join(ROOT, "include", "bitmoe.h")).read()
     assert "int32_t flags;" in header.split("} moe_weights;")[0].split("const void* hot_w2_scales;")[1]
 

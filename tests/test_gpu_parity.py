@@ -260,3 +260,38 @@ def test_empty_batch_is_a_noop(L):
     lg = torch.zeros((0, sp["E"]), dtype=torch.float32, device="cuda")
     res = L.layer_forward(dw, lg, x, sp["k"])
     assert res["out"].shape == (0, sp["H"])
+
+
+# ------------------------------------------------------------------ hot experts as an FP4 residual
+RES_SMALL = {"E": 16, "k": 4, "H": 256, "I": 512, "n_hot": 4}
+
+
+@pytest.mark.parametrize("name,override", [("residual", {}), ("residual", RES_SMALL)])
+def test_residual_dequant_bit_exact(L, name, override):
+    """The streaming kernels' MXFP4 residual decoder (2-bit slot order) gives the MXFP4 weights of
+    every hot slot bit for bit."""
+    sp, dw = device_layer(name, **override)
+    from _helpers import layer_arrays
+
+    _, arrays = layer_arrays(name, **override)
+    for s in (0, sp["n_hot"] - 1):
+        for which in (1, 2):
+            got = host(L.moe_debug_dequant(dw, s, 4 + which)).astype(np.float64)
+            want = OF.dequant_mxfp4(arrays[f"hot_w{which}_codes"][s], arrays[f"hot_w{which}_scales"][s])
+            assert np.array_equal(got, want), (name, s, which, np.argwhere(got != want)[:5])
+
+
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_layer_residual(L, T):
+    _check_layer(L, "residual", T)
+
+
+@pytest.mark.parametrize("T", [1, 16, 100, 300])
+def test_layer_residual_small(L, T):
+    """Hot experts with more than 32 rows (several items each) and, from 128 tokens, cold experts
+    on the grouped GEMM beside hot experts on the streaming kernels."""
+    _check_layer(L, "residual", T, **RES_SMALL)
+
+
+def test_layer_residual_large_batch(L):
+    _check_layer(L, "residual", 4096, sample=True)
