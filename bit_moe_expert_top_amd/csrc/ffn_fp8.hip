@@ -170,27 +170,33 @@ __device__ __forceinline__ uint32_t half_wave_max_u32(uint32_t v) {
 }
 
 // ------------------------------------------------------------------ FP8 grouped GEMM
-constexpr int kF8BM = 128, kF8BN = 128, kF8BK = 128;
+constexpr int kF8BM = 128, kF8BN = 256, kF8BK = 128, kF8Threads = 512;
 constexpr int kF8Row = kF8BK + 16;                  // LDS bytes per tile row (16 B of padding)
-constexpr int kF8Tile = kF8BM * kF8Row;             // one operand tile
-constexpr int kF8Scl = kF8BM * (kF8BK / 32);        // one scale tile (4 bytes per row)
-constexpr int kF8Buf = 2 * kF8Tile + 2 * kF8Scl;    // A, B, their scales
-constexpr int kF8Lds = 2 * kF8Buf;                  // double buffered: 75,776 B
+constexpr int kF8TileA = kF8BM * kF8Row;            // the A (token) tile
+constexpr int kF8TileB = kF8BN * kF8Row;            // the B (weight) tile
+constexpr int kF8SclA = kF8BM * (kF8BK / 32);       // scale tiles (4 bytes per row)
+constexpr int kF8SclB = kF8BN * (kF8BK / 32);
+constexpr int kF8Buf = kF8TileA + kF8TileB + kF8SclA + kF8SclB + 16;  // + a dword for idle threads
+constexpr int kF8Lds = 2 * kF8Buf;                  // double buffered: 113,696 B
 
 __device__ __forceinline__ f32x16_t mfma_scale_32x32x64_fp8(i32x8_t a, i32x8_t b, f32x16_t c, uint32_t sa,
                                                            uint32_t sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, (int)sa, 0, (int)sb);
 }
 
-// Work item = (row tile of <= 128 grouped rows of one hot expert, column tile of 128 weight
-// rows); items of experts outside this batch's slots are skipped.  4 waves (2 x 2), each a
-// 64 x 64 tile of 2 x 2 MFMA 32x32x64 tiles; K steps of 128 through double-buffered LDS.
+// Work item = (row tile of <= 128 grouped rows of one hot expert, column tile of 256 weight
+// rows); items of experts outside this batch's slots are skipped.  8 waves (2 x 4), each a
+// 64 x 64 tile of 2 x 2 MFMA 32x32x64 tiles; one workgroup per CU; K steps of 128 through
+// double-buffered LDS, register-staged two steps ahead.  The 128 x 256 tile reads 384 bytes
+// of operands from L2 per k for 64 K MACs (a 128 x 128 tile: 256 for 16 K).  Within a step the
+// operands of both 64-k sub-steps are read from LDS (two register sets) before the first
+// sub-step's MFMAs, so the second sub-step's LDS latency hides behind them.
 //   FC1: A = MXFP8 x rows gathered by perm / ktop; B = W1 image of the slot (rows [0, 2I));
-//        column tile n: wave column wn holds gate rows 64n + 32wn + [0,32) and up rows
-//        I + 64n + 32wn + [0,32); epilogue h = silu(gate) * up, MXFP8 per 32 columns -> hq.
+//        column tile n: wave column wn holds gate rows 128n + 32wn + [0,32) and up rows
+//        I + 128n + 32wn + [0,32); epilogue h = silu(gate) * up, MXFP8 per 32 columns -> hq.
 //   FC2: A = hq rows r0 ..; B = W2 image (rows [0, H)); epilogue y (fp32).
 template <int FC>
-__global__ __launch_bounds__(256, 2) void fp8_gemm_kernel(
+__global__ __launch_bounds__(kF8Threads, 1) void fp8_gemm_kernel(
     const int32_t* __restrict__ plan, int b0, int S, const uint8_t* __restrict__ slots,
     int64_t slot_bytes, int64_t w_off, int64_t ws_off, int rows_per_expert, int K, int width,
     int ktop, const uint8_t* __restrict__ asrc, const uint8_t* __restrict__ ascale,
@@ -199,10 +205,10 @@ __global__ __launch_bounds__(256, 2) void fp8_gemm_kernel(
   __shared__ __align__(16) uint8_t lds8[kF8Lds];  // static: gfx950 has 160 KB of LDS per CU
   const int tid = threadIdx.x, lane = wave_lane(), w = tid / kWave;
   const int wu = __builtin_amdgcn_readfirstlane(w);  // the wave index as a uniform value
-  const int wm = w & 1, wn = w >> 1, hl = lane >> 5, r32 = lane & 31;
+  const int wm = w & 1, wn = w >> 1, hl = lane >> 5, r32 = lane & 31;  // 2 x 4 waves
   const int n_items = plan[0];
   const int4* items = reinterpret_cast<const int4*>(plan + 4);
-  const int n_ntiles = FC == 1 ? width / 64 : rows_per_expert / kF8BN;
+  const int n_ntiles = FC == 1 ? width / (kF8BN / 2) : rows_per_expert / kF8BN;
   const int total = n_items * n_ntiles;
   const int nk = K / kF8BK, kb32 = K / 32;
 
@@ -219,10 +225,10 @@ __global__ __launch_bounds__(256, 2) void fp8_gemm_kernel(
                                 : make_rsrc(asrc + (int64_t)r0 * K, (uint32_t)nrows * K);
     const buf_rsrc ras = FC == 1 ? make_rsrc(ascale, (uint32_t)(a_rows * kb32))
                                  : make_rsrc(ascale + (int64_t)r0 * kb32, (uint32_t)nrows * kb32);
-    uint32_t aoff[4];
+    uint32_t aoff[2];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r = (tid >> 3) + 32 * u;
+    for (int u = 0; u < 2; ++u) {
+      const int r = (tid >> 3) + 64 * u;
       aoff[u] = kOffNone;
       if (r < nrows) {
         const uint32_t arow = FC == 1 ? (uint32_t)(perm[r0 + r] / ktop) : (uint32_t)r;
@@ -239,7 +245,7 @@ __global__ __launch_bounds__(256, 2) void fp8_gemm_kernel(
     auto wrow_of = [&](int j) {
       if (FC == 1) {
         const int jw = j >> 6, jj = j & 63;
-        return jj < 32 ? 64 * nt_i + 32 * jw + jj : width + 64 * nt_i + 32 * jw + (jj - 32);
+        return jj < 32 ? 128 * nt_i + 32 * jw + jj : width + 128 * nt_i + 32 * jw + (jj - 32);
       }
       return kF8BN * nt_i + j;
     };
@@ -247,41 +253,40 @@ __global__ __launch_bounds__(256, 2) void fp8_gemm_kernel(
     const buf_rsrc rbs = make_rsrc(img + ws_off, (uint32_t)rows_per_expert * kb32);
     uint32_t boff[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) boff[u] = (uint32_t)wrow_of((tid >> 3) + 32 * u) * K + 16u * (tid & 7);
-    const uint32_t bsoff = tid >= 128 ? (uint32_t)wrow_of(tid - 128) * kb32 : kOffNone;
+    for (int u = 0; u < 4; ++u) boff[u] = (uint32_t)wrow_of((tid >> 3) + 64 * u) * K + 16u * (tid & 7);
+    const uint32_t bsoff = (tid >= 128 && tid < 384) ? (uint32_t)wrow_of(tid - 128) * kb32 : kOffNone;
 
     // register staging of K steps, two deep: the loads of step kb + 2 are issued before step kb
     // is computed from LDS; step kb + 1 waits in registers and is stored after the MFMAs
     struct Staged {
-      u32x4 a[4], b[4];
+      u32x4 a[2], b[4];
       uint32_t s;
     };
     Staged stg[2];
     auto load_step = [&](Staged& g, int kb) {
       const uint32_t ko = (uint32_t)kb * kF8BK;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        g.a[u] = buf_load16(ra, aoff[u] + ko);
-        g.b[u] = buf_load16(rb, boff[u] + ko);
-      }
+      for (int u = 0; u < 2; ++u) g.a[u] = buf_load16(ra, aoff[u] + ko);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) g.b[u] = buf_load16(rb, boff[u] + ko);
       // waves 0, 1 (threads 0..127) load the A scales, waves 2, 3 the B scales: the resource is
       // chosen per wave (a per-lane choice of resource makes the compiler loop over both)
-      const bool a_side = wu < 2;
+      const bool a_side = wu < 2;  // waves 2..5: B scales; waves 6, 7 load nothing (kOffNone)
       g.s = buf_load4(a_side ? ras : rbs, (a_side ? asoff : bsoff) + 4u * kb);
     };
     auto store_step = [&](const Staged& g, int buf) {
       uint8_t* la = lds8 + buf * kF8Buf;
-      uint8_t* lb = la + kF8Tile;
-      uint8_t* lsa = lb + kF8Tile;
-      uint8_t* lsb = lsa + kF8Scl;
+      uint8_t* lb = la + kF8TileA;
+      uint8_t* lsa = lb + kF8TileB;
+      uint8_t* lsb = lsa + kF8SclA;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int r = (tid >> 3) + 32 * u;
-        *reinterpret_cast<u32x4*>(la + r * kF8Row + 16 * (tid & 7)) = g.a[u];
-        *reinterpret_cast<u32x4*>(lb + r * kF8Row + 16 * (tid & 7)) = g.b[u];
-      }
-      if (tid < 128) *reinterpret_cast<uint32_t*>(lsa + 4 * tid) = g.s;
-      else *reinterpret_cast<uint32_t*>(lsb + 4 * (tid - 128)) = g.s;
+      for (int u = 0; u < 2; ++u)
+        *reinterpret_cast<u32x4*>(la + ((tid >> 3) + 64 * u) * kF8Row + 16 * (tid & 7)) = g.a[u];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        *reinterpret_cast<u32x4*>(lb + ((tid >> 3) + 64 * u) * kF8Row + 16 * (tid & 7)) = g.b[u];
+      // unconditional stores: threads 384..511 write a scratch dword past the B scales
+      *reinterpret_cast<uint32_t*>(tid < 128 ? lsa + 4 * tid : lsb + 4 * min(tid - 128, 256)) = g.s;
     };
 
     f32x16_t acc[2][2];
@@ -297,13 +302,15 @@ __global__ __launch_bounds__(256, 2) void fp8_gemm_kernel(
       load_step(stg[P], min(kb + 2, nk - 1));  // unconditional (clamped)
       __builtin_amdgcn_sched_barrier(0);
       const uint8_t* la = lds8 + P * kF8Buf;
-      const uint8_t* lb = la + kF8Tile;
-      const uint8_t* lsa = lb + kF8Tile;
-      const uint8_t* lsb = lsa + kF8Scl;
-#pragma unroll
-      for (int kk = 0; kk < kF8BK / 64; ++kk) {
-        i32x8_t av[2], bv[2];
-        uint32_t sa[2], sbv[2];
+      const uint8_t* lb = la + kF8TileA;
+      const uint8_t* lsa = lb + kF8TileB;
+      const uint8_t* lsb = lsa + kF8SclA;
+      // operands of sub-step kk (64 k): the A and B tiles of this wave, their scale bytes
+      struct Ops {
+        i32x8_t a[2], b[2];
+        uint32_t sa[2], sb[2];
+      };
+      auto read_ops = [&](Ops& o, int kk) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const int ra_ = 64 * wm + 32 * t + r32, rb_ = 64 * wn + 32 * t + r32;
@@ -311,16 +318,27 @@ __global__ __launch_bounds__(256, 2) void fp8_gemm_kernel(
           const u32x4 a1 = *reinterpret_cast<const u32x4*>(la + ra_ * kF8Row + 64 * kk + 32 + 16 * hl);
           const u32x4 b0_ = *reinterpret_cast<const u32x4*>(lb + rb_ * kF8Row + 64 * kk + 16 * hl);
           const u32x4 b1_ = *reinterpret_cast<const u32x4*>(lb + rb_ * kF8Row + 64 * kk + 32 + 16 * hl);
-          av[t] = i32x8_t{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-          bv[t] = i32x8_t{(int)b0_[0], (int)b0_[1], (int)b0_[2], (int)b0_[3], (int)b1_[0], (int)b1_[1], (int)b1_[2], (int)b1_[3]};
-          sa[t] = lsa[4 * ra_ + 2 * kk + hl];
-          sbv[t] = lsb[4 * rb_ + 2 * kk + hl];
+          o.a[t] = i32x8_t{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+          o.b[t] = i32x8_t{(int)b0_[0], (int)b0_[1], (int)b0_[2], (int)b0_[3], (int)b1_[0], (int)b1_[1], (int)b1_[2], (int)b1_[3]};
+          o.sa[t] = lsa[4 * ra_ + 2 * kk + hl];
+          o.sb[t] = lsb[4 * rb_ + 2 * kk + hl];
         }
+      };
+      static_assert(kF8BK == 128, "two sub-steps per step");
+      Ops o0, o1;
+      read_ops(o0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      read_ops(o1, 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
-          for (int b = 0; b < 2; ++b) acc[a][b] = mfma_scale_32x32x64_fp8(av[a], bv[b], acc[a][b], sa[a], sbv[b]);
-      }
+        for (int b = 0; b < 2; ++b) acc[a][b] = mfma_scale_32x32x64_fp8(o0.a[a], o0.b[b], acc[a][b], o0.sa[a], o0.sb[b]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = mfma_scale_32x32x64_fp8(o1.a[a], o1.b[b], acc[a][b], o1.sa[a], o1.sb[b]);
       __builtin_amdgcn_sched_barrier(0);  // the store of step kb + 1 after this step's MFMAs
       store_step(stg[P ^ 1], P ^ 1);  // unconditional (at the last step: a clamped reload, unused)
       // LDS writes done, then a bare barrier: step kb + 1 is in LDS for every wave and every wave
@@ -356,7 +374,7 @@ __global__ __launch_bounds__(256, 2) void fp8_gemm_kernel(
           const uint32_t e = f32_to_e4m3_scaled(hb, shared);
           if (row < nrows) {
             const int64_t r = (int64_t)(r0 + row);
-            const int col = 64 * nt_i + 32 * wn + r32;
+            const int col = 128 * nt_i + 32 * wn + r32;
             reinterpret_cast<uint8_t*>(out)[r * width + col] = (uint8_t)e;
             if (r32 == 0) out_scale[r * (width / 32) + col / 32] = (uint8_t)(shared + 127);
           }
@@ -406,9 +424,9 @@ static hipError_t launch_fp8(const int32_t* plan, int b0, int S, const uint8_t* 
                              const uint8_t* asrc, const uint8_t* ascale, const int32_t* perm,
                              int64_t a_rows, int64_t tasks, void* out, uint8_t* out_scale,
                              hipStream_t s) {
-  const int64_t cap = 256 * 2;
+  const int64_t cap = 256;  // one workgroup per CU
   const int grid = (int)(tasks < cap ? (tasks > 0 ? tasks : 1) : cap);
-  fp8_gemm_kernel<FC><<<grid, 256, 0, s>>>(plan, b0, S, slots, slot_bytes, w_off, ws_off, rows, K,
+  fp8_gemm_kernel<FC><<<grid, kF8Threads, 0, s>>>(plan, b0, S, slots, slot_bytes, w_off, ws_off, rows, K,
                                                 width, ktop, asrc, ascale, perm, a_rows, out, out_scale);
   return hipGetLastError();
 }
@@ -418,7 +436,7 @@ hipError_t launch_hot_fc1(int H, int I, int k, int T, const int32_t* hot_plan, i
                           const int32_t* perm, uint8_t* hq, uint8_t* hqs, hipStream_t s) {
   const HotLayout L = hot_layout(H, I);
   return launch_fp8<1>(hot_plan, b0, S, slots, L.slot_bytes, L.w1_off, L.w1s_off, 2 * I, H, I, k, xq, xqs,
-                       perm, T, (int64_t)max_items * (I / 64), hq, hqs, s);
+                       perm, T, (int64_t)max_items * (I / (kF8BN / 2)), hq, hqs, s);
 }
 
 hipError_t launch_hot_fc2(int H, int I, int64_t R, const int32_t* hot_plan, int max_items, int b0,

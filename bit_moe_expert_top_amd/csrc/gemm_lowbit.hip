@@ -16,7 +16,7 @@
 // one barrier per 64-k step; the packed codes and scales run in a four-slot register ring; codes
 // are fetched two steps ahead, token rows three.  Per MFMA the LDS carries
 // 0.5 KB of A reads (no B writes or reads), so the matrix cores rather than LDS bound the step.
-// Work is handed out in blocks of 4 consecutive items x all column tiles, one block to the
+// Work is handed out in blocks of 2 consecutive items x all column tiles, one block to the
 // workgroups of one XCD at a time (workgroups are dispatched to the 8 XCDs round robin), so
 // the weights of a column tile are shared through that XCD's L2 by the block's items (mostly
 // of one expert: items are consecutive row chunks) and an item's token rows by its tiles.
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
   // XCD-aware order: item blocks b = x, x + 8, ... go to XCD x (blockIdx % 8, for a grid that
   // is a multiple of 8); within a block the work runs column tile by column tile, the items of
   // the block side by side
-  constexpr int kIB = 4;  // items per block
+  constexpr int kIB = 2;  // items per block (2 measured faster than 4 and 8)
   const int xcd = blockIdx.x & 7, nb_x = gridDim.x >> 3, lb = blockIdx.x >> 3;
   const int n_blocks = (n_items + kIB - 1) / kIB;
   const int blocks_x = n_blocks > xcd ? (n_blocks - xcd + 7) >> 3 : 0;
