@@ -182,16 +182,26 @@ def measure(sp: dict, dw, T: int, steps: int, warmup: int, flush_between: bool =
     # stream, concurrent with the low-bit stages
     side = torch.cuda.Stream() if sp["n_hot"] > 0 else None
 
+    # small batches: routing, grouping and the FFN's preparation (stage 0) in one launch
+    front = side is None and T <= L.FRONT_MAX_T
+
     def step(evs=None):
         if evs:
             evs[0].record(stream)
-        L.moe_route(logits, k, ids, gw)
-        L.moe_permute(ids, E, ws=ws_p, out=(counts, offsets, perm, inv))
+        if front:
+            if evs:
+                evs[1].record(stream)
+            L.moe_route_permute_prepare(dw, logits, x, k, ws_f, out=(ids, gw, counts, offsets, perm, inv))
+            if evs:
+                evs[2].record(stream)
+        else:
+            L.moe_route(logits, k, ids, gw)
+            L.moe_permute(ids, E, ws=ws_p, out=(counts, offsets, perm, inv))
         stage_evs = {s: (evs[1 + 2 * s], evs[2 + 2 * s]) for s in range(n_stages)} if evs else None
         if side is not None:
             L.moe_expert_ffn_two_streams(dw, x, k, counts, offsets, perm, y, ws_f, side, stage_evs)
         else:
-            for s in range(n_stages):
+            for s in range(1 if front else 0, n_stages):
                 if evs:
                     evs[1 + 2 * s].record(stream)
                 L.moe_expert_ffn_stage(dw, x, k, counts, offsets, perm, y, ws_f, s)
@@ -341,6 +351,7 @@ def measure(sp: dict, dw, T: int, steps: int, warmup: int, flush_between: bool =
         "step_timing": "HIP graph replay" if graph_ms else "eager launches",
         "ms_per_step_eager": eager_ms,
         "hot_convert_overlapped": side is not None,
+        "front_one_launch": front,  # moe_route_permute_prepare instead of route + permute + stage 0
         "stages_ms": {"route+permute+prepare+combine (eager; stage sum for one stream)": eager_ms - fc1_ms - fc2_ms - conv_ms - hot_fc1_ms - hot_fc2_ms,
                       "fc1": fc1_ms, "fc2": fc2_ms, "hot_convert": conv_ms, "hot_fc1": hot_fc1_ms, "hot_fc2": hot_fc2_ms},
         "ffn_stage_ms": [float(np.mean(v)) for v in stage_ms],

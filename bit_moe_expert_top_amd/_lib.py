@@ -55,6 +55,7 @@ _SIGS = {
     "moe_expert_ffn_noalloc": (_i32, [ctypes.POINTER(MoeWeights), _p, _i32, _i32, _p, _p, _p, _p, _p]),
     "moe_expert_ffn_stage": (_i32, [ctypes.POINTER(MoeWeights), _p, _i32, _i32, _p, _p, _p, _p, _p, _sz, _i32,
                                     _p]),
+    "moe_route_permute_prepare": (_i32, [ctypes.POINTER(MoeWeights), _p, _p, _i32, _i32] + [_p] * 7 + [_sz, _p]),
     "moe_combine": (_i32, [_p, _p, _p, _i32, _i32, _i32, _p, _i32, _p]),
     "moe_mxfp4_to_fp8": (_i32, [_p, _p, _i64, _i32, _p, _p, _p]),
     "moe_mxfp8_quantize": (_i32, [_p, _i64, _i32, _p, _p, _p]),
@@ -246,6 +247,28 @@ def moe_expert_ffn_two_streams(w: DeviceWeights, x: torch.Tensor, k: int, counts
     for t in (x, counts, offsets, perm, y_perm, ws):
         t.record_stream(side)
     return y_perm
+
+
+FRONT_MAX_T = 16  # moe_route_permute_prepare takes batches of at most this many tokens
+
+
+def moe_route_permute_prepare(w: DeviceWeights, logits: torch.Tensor, x: torch.Tensor, k: int, ws: torch.Tensor,
+                              out=None):
+    """moe_route + moe_permute + stage 0 of the FFN in one launch (T <= FRONT_MAX_T); returns
+    (topk_ids, topk_w, counts, offsets, perm, inv).  ``ws`` is the FFN workspace."""
+    _dev(logits, torch.float32, "logits")
+    T, E = logits.shape
+    dev = logits.device
+    if out is None:
+        out = (torch.empty((T, k), dtype=torch.int32, device=dev), torch.empty((T, k), dtype=torch.float32, device=dev),
+               torch.empty(E, dtype=torch.int32, device=dev), torch.empty(E + 1, dtype=torch.int32, device=dev),
+               torch.empty(T * k, dtype=torch.int32, device=dev), torch.empty(T * k, dtype=torch.int32, device=dev))
+    ids, gw, counts, offsets, perm, inv = out
+    _check("moe_route_permute_prepare",
+           lib.moe_route_permute_prepare(ctypes.byref(w.c), _ptr(logits), _ptr(x), T, k, _ptr(ids), _ptr(gw),
+                                         _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(inv), _ptr(ws), ws.numel(),
+                                         _stream()))
+    return ids, gw, counts, offsets, perm, inv
 
 
 def moe_combine(y_perm: torch.Tensor, inv: torch.Tensor, topk_w: torch.Tensor, out_fp32: bool = False,

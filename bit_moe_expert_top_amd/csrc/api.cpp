@@ -377,6 +377,51 @@ moe_status moe_expert_ffn_stage(const moe_weights* w, const uint16_t* x, int32_t
   return ffn_run_stage(w, x, T, k, counts, offsets, perm, y_perm, ws, ws_bytes, stage, as_stream(stream));
 }
 
+moe_status moe_route_permute_prepare(const moe_weights* w, const float* logits, const uint16_t* x,
+                                     int32_t T, int32_t k, int32_t* topk_ids, float* topk_w,
+                                     int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                                     void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_weights(w);
+  if (st != MOE_OK) return st;
+  if (T < 0 || k < 1 || k > w->E || k > kMaxTopK) return MOE_ERR_INVALID_ARG;
+  if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
+  if (T > kFrontMaxT) return MOE_ERR_UNSUPPORTED;
+  hipStream_t s = as_stream(stream);
+  if (T == 0) {  // as moe_permute: counts and offsets all zero; nothing else to do
+    hipError_t e1 = launch_fill_i32(counts, w->E, 0, s);
+    hipError_t e2 = launch_fill_i32(offsets, w->E + 1, 0, s);
+    return (e1 == hipSuccess && e2 == hipSuccess) ? MOE_OK : MOE_ERR_HIP;
+  }
+  if (!logits || !x || !topk_ids || !topk_w || !perm || !inv) return MOE_ERR_INVALID_ARG;
+  const FfnLayout L = ffn_layout(w, T, k);
+  if (!ws || ws_bytes < L.fixed) return MOE_ERR_WORKSPACE;
+  if (hot_fp8(w) && ffn_slots(w, L, ws_bytes) < 1) return MOE_ERR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  FrontArgs a{};
+  a.logits = logits;
+  a.T = T;
+  a.E = w->E;
+  a.k = k;
+  a.ids = topk_ids;
+  a.gates = topk_w;
+  a.counts = counts;
+  a.offsets = offsets;
+  a.perm = perm;
+  a.inv = inv;
+  a.small_max = stream_chunk(T);
+  a.gemm_chunk = kGemmRows;
+  a.gemm_enabled = L.gemm ? 1 : 0;
+  a.hot_ids = w->hot_ids;
+  a.n_hot = w->n_hot;
+  a.hot_residual = hot_residual(w) ? 1 : 0;
+  a.plan_s = reinterpret_cast<int32_t*>(base + L.plan_s_off);
+  a.plan_g = reinterpret_cast<int32_t*>(base + L.plan_g_off);
+  a.x = reinterpret_cast<const uint4*>(x);
+  a.fmt = lowbit(w).fmt;
+  a.xp = reinterpret_cast<uint4*>(base + L.xp_off);
+  return from_hip(launch_front(a, w->H, s));
+}
+
 moe_status moe_combine(const float* y_perm, const int32_t* inv, const float* topk_w, int32_t T,
                        int32_t k, int32_t H, void* out, int32_t out_is_fp32, void* stream) {
   if (T < 0 || k < 1 || k > kMaxTopK * 16 || H <= 0 || H % 4) return MOE_ERR_INVALID_ARG;

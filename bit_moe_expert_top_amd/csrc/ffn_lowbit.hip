@@ -27,8 +27,7 @@ size_t plan_bytes(int64_t max_items) { return (size_t)(16 + 16 * max_items); }
 //   work lists (build_plan2): the grouped rows of every low-bit expert, in items of at most
 //   `small_max` rows for the streaming kernel, or (gemm_enabled, groups above small_max) of at
 //   most `gemm_chunk` rows for the grouped GEMM; experts in id order.
-//   2-bit: xp[t][16c + p] = x[t][16c + 4*(p%4) + p/4], one thread per 16 k (byte selects);
-//   3-bit: xp[t][32c + s] = x[t][32c + slot_k(s)], one thread per 32 k.
+//   x in slot order: x_chunk_to_slots (one thread per 16 k for 2-bit, per 32 k for 3-bit).
 __global__ __launch_bounds__(1024) void prepare_kernel(const int32_t* __restrict__ offsets, int E,
                                                        int small_max, int gemm_chunk, int gemm_enabled,
                                                        const int32_t* __restrict__ hot_ids, int n_hot,
@@ -39,40 +38,7 @@ __global__ __launch_bounds__(1024) void prepare_kernel(const int32_t* __restrict
   if (blockIdx.x > 0) {
     const int c = (blockIdx.x - 1) * 1024 + threadIdx.x;
     if (c >= nchunks) return;
-    if (fmt == W2Fmt::kId) {
-      const uint4 a = x[2 * c], b = x[2 * c + 1];  // dwords d0..d3 = a, d4..d7 = b
-      constexpr uint32_t LO = 0x05040100u, HI = 0x07060302u;
-      uint4 o0, o1;
-      o0.x = byte_perm(a.z, a.x, LO);  // (x0, x4)
-      o0.y = byte_perm(b.z, b.x, LO);  // (x8, x12)
-      o0.z = byte_perm(a.z, a.x, HI);  // (x1, x5)
-      o0.w = byte_perm(b.z, b.x, HI);  // (x9, x13)
-      o1.x = byte_perm(a.w, a.y, LO);  // (x2, x6)
-      o1.y = byte_perm(b.w, b.y, LO);  // (x10, x14)
-      o1.z = byte_perm(a.w, a.y, HI);  // (x3, x7)
-      o1.w = byte_perm(b.w, b.y, HI);  // (x11, x15)
-      xp[2 * c] = o0;
-      xp[2 * c + 1] = o1;
-    } else {
-      uint32_t in[16], o[16];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint4 v = x[4 * c + u];
-        in[4 * u] = v.x;
-        in[4 * u + 1] = v.y;
-        in[4 * u + 2] = v.z;
-        in[4 * u + 3] = v.w;
-      }
-#pragma unroll
-      for (int d = 0; d < 16; ++d) {
-        const int k0 = W3Fmt::slot_k(2 * d), k1 = W3Fmt::slot_k(2 * d + 1);
-        const uint32_t lo = (in[k0 >> 1] >> (16 * (k0 & 1))) & 0xFFFFu;
-        const uint32_t hi = (in[k1 >> 1] >> (16 * (k1 & 1))) & 0xFFFFu;
-        o[d] = lo | (hi << 16);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) xp[4 * c + u] = make_uint4(o[4 * u], o[4 * u + 1], o[4 * u + 2], o[4 * u + 3]);
-    }
+    x_chunk_to_slots(x, c, fmt, xp);
     return;
   }
   build_plan2(offsets, E, small_max, gemm_chunk, gemm_enabled, hot_ids, n_hot, hot_residual, plan_s, plan_g);
@@ -132,14 +98,14 @@ __device__ __forceinline__ void load_codes(Pipe<F, NT, G>& P, int slot, int c) {
   for (int t = 0; t < kRT; ++t)
 #pragma unroll
     for (int s = 0; s < G; ++s)
-      P.cw[slot][s][t] = F::load_codes(P.rc, P.coff[t] + F::code_bytes(256u * G * (uint32_t)c + 64u * (uint32_t)s));
+      P.cw[slot][s][t] = F::load_codes_s(P.rc, P.coff[t], F::code_bytes(256u * G * (uint32_t)c + 64u * (uint32_t)s));
 }
 
 template <class F, int NT, int G>
 __device__ __forceinline__ void load_scales(Pipe<F, NT, G>& P, int c) {
 #pragma unroll
   for (int t = 0; t < kRT; ++t)
-    P.sc_next[t] = load_scale_bytes<Pipe<F, NT, G>::SB>(P.rs, P.soff[t] + F::scale_bytes(256u * G * (uint32_t)c));
+    P.sc_next[t] = load_scale_bytes_s<Pipe<F, NT, G>::SB>(P.rs, P.soff[t], F::scale_bytes(256u * G * (uint32_t)c));
 }
 
 // The weight resources of one expert (or one hot slot of the residual arrays) and this lane's
@@ -171,7 +137,7 @@ __device__ __forceinline__ void dma_b(buf_rsrc rb, uint8_t* stage, const uint32_
   for (int u = 0; u < 8; ++u)
     if (active & (1u << u))
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(stage + 16 * (256 * u + 64 * wu)), 16,
-                                               (int)(doff[u] + ko), 0, 0, 0);
+                                               (int)doff[u], (int)ko, 0, 0);
 }
 
 // s_waitcnt vmcnt(N) on gfx9: vmcnt in bits [3:0] and [15:14]; expcnt (bits [6:4]) and lgkmcnt

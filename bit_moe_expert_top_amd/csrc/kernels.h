@@ -51,6 +51,24 @@ hipError_t launch_prepare(const int32_t* offsets, int E, int small_max, int gemm
                           int32_t* plan_g, const uint16_t* x, int T, int H, int fmt, uint16_t* xp,
                           hipStream_t s);
 
+// Routing, grouping and stage 0 of the FFN in one launch (front.hip), for T <= kFrontMaxT and
+// R = T*k <= kPermuteChunk.  nchunks and nbits are set by launch_front.
+constexpr int kFrontMaxT = 16;
+struct FrontArgs {
+  const float* logits;
+  int T, E, k, nbits;
+  int32_t *ids, *counts, *offsets, *perm, *inv;
+  float* gates;
+  int small_max, gemm_chunk, gemm_enabled;
+  const int32_t* hot_ids;
+  int n_hot, hot_residual;
+  int32_t *plan_s, *plan_g;
+  const uint4* x;
+  int nchunks, fmt;
+  uint4* xp;
+};
+hipError_t launch_front(const FrontArgs& a, int H, hipStream_t s);
+
 // Decode-style kernels: weight-streaming, MFMA on 16-token tiles.
 // split_T: the batch size the K split across a workgroup's waves is chosen for (T itself, or 1
 // for a split that does not depend on the batch)

@@ -24,6 +24,28 @@ struct ScaleBytes {
   uint32_t v[NB >= 4 ? NB / 4 : 1];
 };
 template <int NB>
+__device__ __forceinline__ ScaleBytes<NB> load_scale_bytes_s(buf_rsrc r, uint32_t off, uint32_t soff) {
+  ScaleBytes<NB> s;
+  if constexpr (NB == 1) {
+    s.v[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)off, (int)soff, 0);
+  } else if constexpr (NB == 2) {
+    s.v[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, (int)soff, 0);
+  } else if constexpr (NB == 4) {
+    s.v[0] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, (int)soff, 0);
+  } else if constexpr (NB == 8) {
+    const uint64_t t = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, (int)soff, 0));
+    s.v[0] = (uint32_t)t;
+    s.v[1] = (uint32_t)(t >> 32);
+  } else {
+    const u32x4 t = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, (int)soff, 0));
+    s.v[0] = t[0];
+    s.v[1] = t[1];
+    s.v[2] = t[2];
+    s.v[3] = t[3];
+  }
+  return s;
+}
+template <int NB>
 __device__ __forceinline__ ScaleBytes<NB> load_scale_bytes(buf_rsrc r, uint32_t off) {
   ScaleBytes<NB> s;
   if constexpr (NB == 1) {
@@ -71,6 +93,9 @@ struct W2Fmt {
   struct Tab { uint32_t lut[2], sw; };
 
   __device__ static __forceinline__ Codes load_codes(buf_rsrc r, uint32_t off) { return {buf_load16(r, off)}; }
+  __device__ static __forceinline__ Codes load_codes_s(buf_rsrc r, uint32_t off, uint32_t soff) {
+    return {buf_load16s(r, off, soff)};
+  }
 
   // high bytes {-4s, -s, s, 4s} of group g: bytes (hb^0x80)+1, hb^0x80, hb, hb+1 (the sign
   // flip, the exponent +2 in the high byte); x = sw with both sign bits flipped
@@ -162,6 +187,14 @@ struct W3Fmt {
   struct Codes { u32x4 a; uint32_t b0, b1; };
   struct Tab { uint32_t hb1, hb0, lb1, lb0; };
 
+  __device__ static __forceinline__ Codes load_codes_s(buf_rsrc r, uint32_t off, uint32_t soff) {
+    Codes c;
+    c.a = buf_load16s(r, off, soff);
+    const uint64_t t = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(r, (int)(off + 16u), (int)soff, 0));
+    c.b0 = (uint32_t)t;
+    c.b1 = (uint32_t)(t >> 32);
+    return c;
+  }
   __device__ static __forceinline__ Codes load_codes(buf_rsrc r, uint32_t off) {
     Codes c;
     c.a = buf_load16(r, off);
@@ -277,6 +310,9 @@ struct Fp4Fmt {
   __device__ static __forceinline__ Codes load_codes(buf_rsrc r, uint32_t off) {
     return {buf_load16(r, off), buf_load16(r, off + 16u)};
   }
+  __device__ static __forceinline__ Codes load_codes_s(buf_rsrc r, uint32_t off, uint32_t soff) {
+    return {buf_load16s(r, off, soff), buf_load16s(r, off + 16u, soff)};
+  }
   __device__ static __forceinline__ GTab group_table(uint32_t e) {
     // bf16 bits of the magnitudes at scale 1, in pairs; + (e - 127) << 7 on every nonzero one
     const uint16_t x = (uint16_t)((e - 127u) << 7);
@@ -326,5 +362,48 @@ struct Fp4Fmt {
   __host__ __device__ static constexpr int pos32(int c) { return W2Fmt::pos32(c); }
   __host__ __device__ static constexpr int slot_k(int s) { return W2Fmt::slot_k(s); }
 };
+
+
+// x stored in the k-slot order of the weight format (the token operand of the low-bit FFN
+// kernels), one chunk per thread:
+//   2-bit: xp[t][16c + p] = x[t][16c + 4*(p%4) + p/4] for chunk c of 16 k (byte selects);
+//   3-bit: xp[t][32c + s] = x[t][32c + slot_k(s)] for chunk c of 32 k.
+__device__ __forceinline__ void x_chunk_to_slots(const uint4* __restrict__ x, int c, int fmt,
+                                                 uint4* __restrict__ xp) {
+  if (fmt == W2Fmt::kId) {
+    const uint4 a = x[2 * c], b = x[2 * c + 1];  // dwords d0..d3 = a, d4..d7 = b
+    constexpr uint32_t LO = 0x05040100u, HI = 0x07060302u;
+    uint4 o0, o1;
+    o0.x = byte_perm(a.z, a.x, LO);  // (x0, x4)
+    o0.y = byte_perm(b.z, b.x, LO);  // (x8, x12)
+    o0.z = byte_perm(a.z, a.x, HI);  // (x1, x5)
+    o0.w = byte_perm(b.z, b.x, HI);  // (x9, x13)
+    o1.x = byte_perm(a.w, a.y, LO);  // (x2, x6)
+    o1.y = byte_perm(b.w, b.y, LO);  // (x10, x14)
+    o1.z = byte_perm(a.w, a.y, HI);  // (x3, x7)
+    o1.w = byte_perm(b.w, b.y, HI);  // (x11, x15)
+    xp[2 * c] = o0;
+    xp[2 * c + 1] = o1;
+  } else {
+    uint32_t in[16], o[16];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint4 v = x[4 * c + u];
+      in[4 * u] = v.x;
+      in[4 * u + 1] = v.y;
+      in[4 * u + 2] = v.z;
+      in[4 * u + 3] = v.w;
+    }
+#pragma unroll
+    for (int d = 0; d < 16; ++d) {
+      const int k0 = W3Fmt::slot_k(2 * d), k1 = W3Fmt::slot_k(2 * d + 1);
+      const uint32_t lo = (in[k0 >> 1] >> (16 * (k0 & 1))) & 0xFFFFu;
+      const uint32_t hi = (in[k1 >> 1] >> (16 * (k1 & 1))) & 0xFFFFu;
+      o[d] = lo | (hi << 16);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) xp[4 * c + u] = make_uint4(o[4 * u], o[4 * u + 1], o[4 * u + 2], o[4 * u + 3]);
+  }
+}
 
 }  // namespace bitmoe

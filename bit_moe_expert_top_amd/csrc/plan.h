@@ -45,22 +45,23 @@ __device__ __forceinline__ void build_plan(const int32_t* __restrict__ offsets, 
 
 namespace bitmoe {
 
-// Two work lists in one pass (one block of 1024 threads), for batches that use both FFN
+// Two work lists in one pass (one block of NT threads), for batches that use both FFN
 // kernels: a low-bit expert with more than `small_max` rows goes to the grouped-GEMM list in
 // items of at most `gemm_chunk` rows; one with fewer goes to the streaming list in items of at
 // most `small_max` rows.  With gemm_enabled == 0 every expert goes to the streaming list.  Hot
 // experts are left out, unless hot_residual: then they go to the streaming list at any size,
 // each item carrying the expert's hot slot (the FP4 residual the streaming kernel adds).  Both
 // lists have the layout of build_plan.
+template <int NT = 1024>
 __device__ __forceinline__ void build_plan2(const int32_t* __restrict__ offsets, int E, int small_max,
                                             int gemm_chunk, int gemm_enabled,
                                             const int32_t* __restrict__ hot_ids, int n_hot, int hot_residual,
                                             int32_t* __restrict__ plan_s, int32_t* __restrict__ plan_g) {
-  __shared__ int scan_tmp[1024 / kWave + 1];
-  __shared__ int16_t slot_of[1024];
-  for (int e = threadIdx.x; e < E; e += 1024) slot_of[e] = -1;
+  __shared__ int scan_tmp[NT / kWave + 1];
+  __shared__ int16_t slot_of[1024];  // E <= 1024
+  for (int e = threadIdx.x; e < E; e += NT) slot_of[e] = -1;
   __syncthreads();
-  for (int s = threadIdx.x; s < n_hot; s += 1024) {
+  for (int s = threadIdx.x; s < n_hot; s += NT) {
     const int he = hot_ids[s];
     if ((unsigned)he < (unsigned)E) slot_of[he] = (int16_t)s;  // ids outside [0, E) are ignored
   }
@@ -68,7 +69,7 @@ __device__ __forceinline__ void build_plan2(const int32_t* __restrict__ offsets,
   int4* items_s = reinterpret_cast<int4*>(plan_s + 4);
   int4* items_g = reinterpret_cast<int4*>(plan_g + 4);
   int run_s = 0, run_g = 0;
-  for (int e0 = 0; e0 < E; e0 += 1024) {
+  for (int e0 = 0; e0 < E; e0 += NT) {
     const int e = e0 + threadIdx.x;
     int cnt = 0, slot = -1;
     if (e < E) {
@@ -79,8 +80,8 @@ __device__ __forceinline__ void build_plan2(const int32_t* __restrict__ offsets,
     const int chunk = big ? gemm_chunk : small_max;
     const int nch = (cnt + chunk - 1) / chunk;
     int tot_s, tot_g;
-    const int ex_s = block_exclusive_scan<1024>(big ? 0 : nch, scan_tmp, &tot_s);
-    const int ex_g = block_exclusive_scan<1024>(big ? nch : 0, scan_tmp, &tot_g);
+    const int ex_s = block_exclusive_scan<NT>(big ? 0 : nch, scan_tmp, &tot_s);
+    const int ex_g = block_exclusive_scan<NT>(big ? nch : 0, scan_tmp, &tot_g);
     int4* dst = big ? items_g + run_g + ex_g : items_s + run_s + ex_s;
     for (int c = 0; c < nch; ++c) dst[c] = make_int4(e, offsets[e] + c * chunk, min(chunk, cnt - c * chunk), slot);
     run_s += tot_s;

@@ -155,3 +155,25 @@ def test_quantizer_argument_checks(lib):
         assert f(None, 4, 64, p, p, None) == -1   # null input
         assert f(p, 4, 64, p, None, None) == -1   # null output
         assert f(None, 0, 64, None, None, None) == 0  # rows = 0 is a no-op
+
+
+def test_front_argument_checks(lib):
+    """moe_route_permute_prepare rejects bad arguments on the host; batches above 16 tokens are
+    UNSUPPORTED (the caller runs the three calls instead)."""
+    import sys
+    sys.path.insert(0, ROOT)
+    from bit_moe_expert_top_amd import _lib as L
+
+    p = 16
+    w = L.MoeWeights(8, 256, 512, L.MOE_FMT_W2, p, p, p, p, 0, None, None, None, None, None)
+    f = L.lib.moe_route_permute_prepare
+    args = lambda T, k, ws_bytes=1 << 30, counts=p: (ctypes.byref(w), p, p, T, k, p, p, counts, p, p, p, p,
+                                                      ws_bytes, None)
+    assert f(*args(17, 2)) == -2                 # more than 16 tokens: not this call
+    assert f(*args(4, 0)) == -1                  # k < 1
+    assert f(*args(4, 9)) == -1                  # k > E
+    assert f(*args(-1, 2)) == -1                 # T < 0
+    assert f(*args(4, 2, counts=None)) == -1     # null output
+    assert f(*args(4, 2, ws_bytes=10)) == -3     # workspace too small
+    bad = L.MoeWeights(8, 200, 512, L.MOE_FMT_W2, p, p, p, p, 0, None, None, None, None, None)
+    assert f(ctypes.byref(bad), p, p, 4, 2, p, p, p, p, p, p, p, 1 << 30, None) == -1
