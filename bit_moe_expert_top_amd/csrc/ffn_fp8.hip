@@ -171,26 +171,43 @@ __device__ __forceinline__ uint32_t half_wave_max_u32(uint32_t v) {
 
 // ------------------------------------------------------------------ FP8 grouped GEMM
 constexpr int kF8BM = 128, kF8BN = 256, kF8BK = 128, kF8Threads = 512;
-constexpr int kF8Row = kF8BK + 16;                  // LDS bytes per tile row (16 B of padding)
-constexpr int kF8TileA = kF8BM * kF8Row;            // the A (token) tile
-constexpr int kF8TileB = kF8BN * kF8Row;            // the B (weight) tile
-constexpr int kF8SclA = kF8BM * (kF8BK / 32);       // scale tiles (4 bytes per row)
-constexpr int kF8SclB = kF8BN * (kF8BK / 32);
-constexpr int kF8Buf = kF8TileA + kF8TileB + kF8SclA + kF8SclB + 16;  // + a dword for idle threads
-constexpr int kF8Lds = 2 * kF8Buf;                  // double buffered: 113,696 B
+// One K step of the workgroup tile in LDS: A (token) and B (weight) rows of 128 bytes whose
+// 16-byte chunks sit XOR-swizzled by the row (chunk c of row r at position c ^ ((r / 2) % 8):
+// the LDS serves a 128-bit read 16 lanes at a time across 64 banks, i.e. two 128-byte rows, so
+// one chunk read from 16 consecutive rows hits 16 different bank groups), then the e8m0 scales
+// (4 bytes per row), then a pad that the idle lanes' scale loads write into.
+constexpr int kF8TileA = kF8BM * kF8BK;             // 16 KB
+constexpr int kF8TileB = kF8BN * kF8BK;             // 32 KB
+constexpr int kF8SclA = kF8BM * (kF8BK / 32);       // 512 B
+constexpr int kF8SclB = kF8BN * (kF8BK / 32);       // 1 KB
+constexpr int kF8Pad = 2 * 256;                     // waves 6, 7: one 256-byte scale load each
+constexpr int kF8Stage = kF8TileA + kF8TileB + kF8SclA + kF8SclB + kF8Pad;  // 50,688 B
+constexpr int kF8Loads = 7;  // direct loads per wave and step: 2 A, 4 B, 1 scale
 
 __device__ __forceinline__ f32x16_t mfma_scale_32x32x64_fp8(i32x8_t a, i32x8_t b, f32x16_t c, uint32_t sa,
                                                            uint32_t sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, (int)sa, 0, (int)sb);
 }
 
+typedef __attribute__((address_space(3))) void lds8_void;
+
+// The operands of one 64-k sub-step for one wave: its two A and two B 32-row tiles (32 bytes
+// per lane) and their scale bytes.
+struct F8Sub {
+  i32x8_t a[2], b[2];
+  uint32_t sa[2], sb[2];
+};
+
 // Work item = (row tile of <= 128 grouped rows of one hot expert, column tile of 256 weight
 // rows); items of experts outside this batch's slots are skipped.  8 waves (2 x 4), each a
-// 64 x 64 tile of 2 x 2 MFMA 32x32x64 tiles; one workgroup per CU; K steps of 128 through
-// double-buffered LDS, register-staged two steps ahead.  The 128 x 256 tile reads 384 bytes
-// of operands from L2 per k for 64 K MACs (a 128 x 128 tile: 256 for 16 K).  Within a step the
-// operands of both 64-k sub-steps are read from LDS (two register sets) before the first
-// sub-step's MFMAs, so the second sub-step's LDS latency hides behind them.
+// 64 x 64 tile of 2 x 2 MFMA 32x32x64 tiles; one workgroup per CU.  K steps of 128 run through
+// a ring of three LDS stages filled by direct global -> LDS loads (no registers, no LDS store
+// instructions), two steps ahead.  At step kb a wave waits for its own loads of stage kb+1 and
+// for its reads of stage kb, meets the others at one barrier (stage kb+1 is complete and stage
+// kb's buffer is free), refills that buffer with stage kb+3, reads stage kb+1's operands into
+// its second register set and then issues stage kb's MFMAs: the LDS reads of the next step run
+// while the matrix cores work on this one.  The 128 x 256 tile reads 384 bytes of operands from
+// L2 per k for 64 K MACs.
 //   FC1: A = MXFP8 x rows gathered by perm / ktop; B = W1 image of the slot (rows [0, 2I));
 //        column tile n: wave column wn holds gate rows 128n + 32wn + [0,32) and up rows
 //        I + 128n + 32wn + [0,32); epilogue h = silu(gate) * up, MXFP8 per 32 columns -> hq.
@@ -202,7 +219,11 @@ __global__ __launch_bounds__(kF8Threads, 1) void fp8_gemm_kernel(
     int ktop, const uint8_t* __restrict__ asrc, const uint8_t* __restrict__ ascale,
     const int32_t* __restrict__ perm, int64_t a_rows, void* __restrict__ out,
     uint8_t* __restrict__ out_scale) {
-  __shared__ __align__(16) uint8_t lds8[kF8Lds];  // static: gfx950 has 160 KB of LDS per CU
+  // three stages as separate objects, so that waiting for one stage's loads does not wait for
+  // the others' (gfx950 has 160 KB of LDS per CU)
+  __shared__ __align__(16) uint8_t st0[kF8Stage];
+  __shared__ __align__(16) uint8_t st1[kF8Stage];
+  __shared__ __align__(16) uint8_t st2[kF8Stage];
   const int tid = threadIdx.x, lane = wave_lane(), w = tid / kWave;
   const int wu = __builtin_amdgcn_readfirstlane(w);  // the wave index as a uniform value
   const int wm = w & 1, wn = w >> 1, hl = lane >> 5, r32 = lane & 31;  // 2 x 4 waves
@@ -220,7 +241,9 @@ __global__ __launch_bounds__(kF8Threads, 1) void fp8_gemm_kernel(
     const int r0 = itm.y, nrows = itm.z;
     const uint8_t* img = slots + (int64_t)slot * slot_bytes;
 
-    // A rows: thread owns 16-byte chunks (tid & 7) of rows (tid >> 3) + 32u
+    // direct loads: round u of wave w fills LDS bytes [1024 (8u + w), +1024) of a tile, i.e.
+    // rows 8 (8u + w) + lane / 8, position lane % 8, which holds chunk (lane % 8) ^ ((row / 2) % 8)
+    const int prow = lane >> 3, ppos = lane & 7;
     const buf_rsrc ra = FC == 1 ? make_rsrc(asrc, (uint32_t)(a_rows * K))
                                 : make_rsrc(asrc + (int64_t)r0 * K, (uint32_t)nrows * K);
     const buf_rsrc ras = FC == 1 ? make_rsrc(ascale, (uint32_t)(a_rows * kb32))
@@ -228,18 +251,12 @@ __global__ __launch_bounds__(kF8Threads, 1) void fp8_gemm_kernel(
     uint32_t aoff[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int r = (tid >> 3) + 64 * u;
+      const int r = 8 * (8 * u + w) + prow;
       aoff[u] = kOffNone;
       if (r < nrows) {
         const uint32_t arow = FC == 1 ? (uint32_t)(perm[r0 + r] / ktop) : (uint32_t)r;
-        aoff[u] = arow * (uint32_t)K + 16u * (tid & 7);
+        aoff[u] = arow * (uint32_t)K + 16u * (uint32_t)(ppos ^ ((r >> 1) & 7));
       }
-    }
-    // A scales: threads 0..127 own row tid; B scales: threads 128..255 own row tid - 128
-    uint32_t asoff = kOffNone;
-    if (tid < 128 && tid < nrows) {
-      const uint32_t arow = FC == 1 ? (uint32_t)(perm[r0 + tid] / ktop) : (uint32_t)tid;
-      asoff = arow * (uint32_t)kb32;
     }
     // B rows of the tile (LDS row j -> weight row)
     auto wrow_of = [&](int j) {
@@ -253,40 +270,66 @@ __global__ __launch_bounds__(kF8Threads, 1) void fp8_gemm_kernel(
     const buf_rsrc rbs = make_rsrc(img + ws_off, (uint32_t)rows_per_expert * kb32);
     uint32_t boff[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) boff[u] = (uint32_t)wrow_of((tid >> 3) + 64 * u) * K + 16u * (tid & 7);
-    const uint32_t bsoff = (tid >= 128 && tid < 384) ? (uint32_t)wrow_of(tid - 128) * kb32 : kOffNone;
+    for (int u = 0; u < 4; ++u) {
+      const int j = 8 * (8 * u + w) + prow;
+      boff[u] = (uint32_t)wrow_of(j) * K + 16u * (uint32_t)(ppos ^ ((j >> 1) & 7));
+    }
+    // scale loads (4 bytes per lane = one row's four e8m0 scales of the step): waves 0, 1 the A
+    // rows 64w + lane, waves 2..5 the B rows 64(w - 2) + lane, waves 6, 7 nothing (kOffNone)
+    const bool a_side = wu < 2;
+    uint32_t soff = kOffNone;
+    if (w < 2) {
+      const int r = 64 * w + lane;
+      if (r < nrows) soff = (FC == 1 ? (uint32_t)(perm[r0 + r] / ktop) : (uint32_t)r) * (uint32_t)kb32;
+    } else if (w < 6) {
+      soff = (uint32_t)wrow_of(64 * (w - 2) + lane) * (uint32_t)kb32;
+    }
+    // LDS offset of this wave's scale load within a stage
+    const int sdst = kF8TileA + kF8TileB + 256 * w;
 
-    // register staging of K steps, two deep: the loads of step kb + 2 are issued before step kb
-    // is computed from LDS; step kb + 1 waits in registers and is stored after the MFMAs
-    struct Staged {
-      u32x4 a[2], b[4];
-      uint32_t s;
-    };
-    Staged stg[2];
-    auto load_step = [&](Staged& g, int kb) {
-      const uint32_t ko = (uint32_t)kb * kF8BK;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) g.a[u] = buf_load16(ra, aoff[u] + ko);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) g.b[u] = buf_load16(rb, boff[u] + ko);
-      // waves 0, 1 (threads 0..127) load the A scales, waves 2, 3 the B scales: the resource is
-      // chosen per wave (a per-lane choice of resource makes the compiler loop over both)
-      const bool a_side = wu < 2;  // waves 2..5: B scales; waves 6, 7 load nothing (kOffNone)
-      g.s = buf_load4(a_side ? ras : rbs, (a_side ? asoff : bsoff) + 4u * kb);
-    };
-    auto store_step = [&](const Staged& g, int buf) {
-      uint8_t* la = lds8 + buf * kF8Buf;
-      uint8_t* lb = la + kF8TileA;
-      uint8_t* lsa = lb + kF8TileB;
-      uint8_t* lsb = lsa + kF8SclA;
+    auto stage_ptr = [&](int s) -> uint8_t* { return s == 0 ? st0 : (s == 1 ? st1 : st2); };
+    // the loads of step kb (clamped to the last step: the copies past the end are never read)
+    // into stage buffer s
+    auto load_stage = [&](int s, int kb) {
+      uint8_t* st = stage_ptr(s);
+      const uint32_t ko = (uint32_t)min(kb, nk - 1) * kF8BK;
 #pragma unroll
       for (int u = 0; u < 2; ++u)
-        *reinterpret_cast<u32x4*>(la + ((tid >> 3) + 64 * u) * kF8Row + 16 * (tid & 7)) = g.a[u];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds8_void*)(st + 1024 * (8 * u + wu)), 16, (int)aoff[u],
+                                                 (int)ko, 0, 0);
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        *reinterpret_cast<u32x4*>(lb + ((tid >> 3) + 64 * u) * kF8Row + 16 * (tid & 7)) = g.b[u];
-      // unconditional stores: threads 384..511 write a scratch dword past the B scales
-      *reinterpret_cast<uint32_t*>(tid < 128 ? lsa + 4 * tid : lsb + 4 * min(tid - 128, 256)) = g.s;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds8_void*)(st + kF8TileA + 1024 * (8 * u + wu)), 16,
+                                                 (int)boff[u], (int)ko, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_side ? ras : rbs, (lds8_void*)(st + sdst), 4, (int)soff,
+                                               (int)(ko / 32), 0, 0);
+    };
+    // this wave's operands of sub-step kk of a step from stage buffer s.  Tile rows 64 wm + 32 t
+    // + r32 have (row / 2) % 8 == (r32 / 2) % 8, so the swizzled position of chunk c is the same
+    // for every tile: per lane four chunk offsets (c = hl, 2 + hl, 4 + hl, 6 + hl) and a row base,
+    // the rest are instruction offsets.
+    uint32_t cofs[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cofs[j] = 16u * (uint32_t)((2 * j + hl) ^ ((r32 >> 1) & 7));
+    const uint32_t abase = 128u * (uint32_t)(64 * wm + r32), bbase = 128u * (uint32_t)(64 * wn + r32);
+    const uint32_t sabase = 4u * (uint32_t)(64 * wm + r32) + hl, sbbase = 4u * (uint32_t)(64 * wn + r32) + hl;
+    auto read_sub = [&](F8Sub& o, int s, int kk) {
+      const uint8_t* la = stage_ptr(s);
+      const uint8_t* lb = la + kF8TileA;
+      const uint8_t* lsa = lb + kF8TileB;
+      const uint8_t* lsb = lsa + kF8SclA;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(la + abase + cofs[2 * kk] + 4096 * t);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(la + abase + cofs[2 * kk + 1] + 4096 * t);
+        const u32x4 b0_ = *reinterpret_cast<const u32x4*>(lb + bbase + cofs[2 * kk] + 4096 * t);
+        const u32x4 b1_ = *reinterpret_cast<const u32x4*>(lb + bbase + cofs[2 * kk + 1] + 4096 * t);
+        o.a[t] = i32x8_t{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+        o.b[t] = i32x8_t{(int)b0_[0], (int)b0_[1], (int)b0_[2], (int)b0_[3], (int)b1_[0], (int)b1_[1], (int)b1_[2],
+                         (int)b1_[3]};
+        o.sa[t] = lsa[sabase + 128 * t + 2 * kk];
+        o.sb[t] = lsb[sbbase + 128 * t + 2 * kk];
+      }
     };
 
     f32x16_t acc[2][2];
@@ -296,66 +339,59 @@ __global__ __launch_bounds__(kF8Threads, 1) void fp8_gemm_kernel(
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
-
-    auto iter = [&](auto P_, int kb) {
-      constexpr int P = decltype(P_)::value;
-      load_step(stg[P], min(kb + 2, nk - 1));  // unconditional (clamped)
-      __builtin_amdgcn_sched_barrier(0);
-      const uint8_t* la = lds8 + P * kF8Buf;
-      const uint8_t* lb = la + kF8TileA;
-      const uint8_t* lsa = lb + kF8TileB;
-      const uint8_t* lsb = lsa + kF8SclA;
-      // operands of sub-step kk (64 k): the A and B tiles of this wave, their scale bytes
-      struct Ops {
-        i32x8_t a[2], b[2];
-        uint32_t sa[2], sb[2];
-      };
-      auto read_ops = [&](Ops& o, int kk) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int ra_ = 64 * wm + 32 * t + r32, rb_ = 64 * wn + 32 * t + r32;
-          const u32x4 a0 = *reinterpret_cast<const u32x4*>(la + ra_ * kF8Row + 64 * kk + 16 * hl);
-          const u32x4 a1 = *reinterpret_cast<const u32x4*>(la + ra_ * kF8Row + 64 * kk + 32 + 16 * hl);
-          const u32x4 b0_ = *reinterpret_cast<const u32x4*>(lb + rb_ * kF8Row + 64 * kk + 16 * hl);
-          const u32x4 b1_ = *reinterpret_cast<const u32x4*>(lb + rb_ * kF8Row + 64 * kk + 32 + 16 * hl);
-          o.a[t] = i32x8_t{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-          o.b[t] = i32x8_t{(int)b0_[0], (int)b0_[1], (int)b0_[2], (int)b0_[3], (int)b1_[0], (int)b1_[1], (int)b1_[2], (int)b1_[3]};
-          o.sa[t] = lsa[4 * ra_ + 2 * kk + hl];
-          o.sb[t] = lsb[4 * rb_ + 2 * kk + hl];
-        }
-      };
-      static_assert(kF8BK == 128, "two sub-steps per step");
-      Ops o0, o1;
-      read_ops(o0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      read_ops(o1, 1);
-      __builtin_amdgcn_sched_barrier(0);
+    // The MFMA builtins are pure, so the optimizer may sink them past the barriers and reads
+    // that follow (and keep every operand live until then): an empty volatile asm that reads the
+    // accumulators keeps each sub-step's MFMAs where they are issued.
+    auto mfma_sub = [&](const F8Sub& o) {
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = mfma_scale_32x32x64_fp8(o0.a[a], o0.b[b], acc[a][b], o0.sa[a], o0.sb[b]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = mfma_scale_32x32x64_fp8(o1.a[a], o1.b[b], acc[a][b], o1.sa[a], o1.sb[b]);
-      __builtin_amdgcn_sched_barrier(0);  // the store of step kb + 1 after this step's MFMAs
-      store_step(stg[P ^ 1], P ^ 1);  // unconditional (at the last step: a clamped reload, unused)
-      // LDS writes done, then a bare barrier: step kb + 1 is in LDS for every wave and every wave
-      // is done with buffer P.  (A __syncthreads fence would also drain the loads of step kb + 2
-      // issued above, which are only needed at the end of the next step.)
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt not waited on
-      asm volatile("s_barrier" ::: "memory");
+        for (int b = 0; b < 2; ++b) acc[a][b] = mfma_scale_32x32x64_fp8(o.a[a], o.b[b], acc[a][b], o.sa[a], o.sb[b]);
+      asm volatile("" ::"v"(acc[0][0]), "v"(acc[0][1]), "v"(acc[1][0]), "v"(acc[1][1]));
     };
 
-    load_step(stg[0], 0);
-    load_step(stg[1], min(1, nk - 1));
-    store_step(stg[0], 0);
-    __syncthreads();
-    for (int kb = 0; kb < nk; kb += 2) {  // nk is even (K is a multiple of 256)
-      iter(std::integral_constant<int, 0>{}, kb);
-      iter(std::integral_constant<int, 1>{}, kb + 1);
+    // Step kb (stage kb in buffer D; sub-step 0's operands already in s0):
+    //   read sub-step 1 into s1; MFMAs of sub-step 0;
+    //   wait for this wave's loads of stage kb+1 and its reads of stage kb; barrier: stage kb+1
+    //   is complete and nobody reads buffer D any more; load stage kb+3 into D;
+    //   read sub-step 0 of step kb+1 into s0; MFMAs of sub-step 1.
+    F8Sub s0, s1;
+    auto step = [&](auto D_, int kb) {
+      constexpr int D = decltype(D_)::value;
+      read_sub(s1, D, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_sub(s0);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt((kF8Loads & 15) | 0x70 | ((kF8Loads >> 4) << 14));  // vmcnt(7), lgkmcnt(0)
+      asm volatile("s_barrier" ::: "memory");
+      load_stage(D, kb + 3);
+      if (kb + 1 < nk) read_sub(s0, (D + 1) % 3, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_sub(s1);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    load_stage(0, 0);
+    load_stage(1, 1);
+    load_stage(2, 2);
+    __builtin_amdgcn_s_waitcnt((2 * kF8Loads & 15) | 0x70 | 0xF00 | (((2 * kF8Loads) >> 4) << 14));  // vmcnt(14)
+    asm volatile("s_barrier" ::: "memory");  // stage 0 is complete for every wave
+    read_sub(s0, 0, 0);
+    int kb = 0;
+    for (; kb + 3 <= nk; kb += 3) {
+      step(I0{}, kb);
+      step(I1{}, kb + 1);
+      step(I2{}, kb + 2);
     }
+    if (kb < nk) step(I0{}, kb);  // 0, 1 or 2 steps remain, from buffer 0
+    if (kb + 1 < nk) step(I1{}, kb + 1);
+    // every wave is done with the stage buffers before the next task's loads (and the loads of
+    // stages past the end, which nobody reads, have landed)
+    __builtin_amdgcn_s_waitcnt(0xC07F & ~0xC00F);  // vmcnt(0), lgkmcnt(0)
+    __syncthreads();
 
     // ---- epilogue
 #pragma unroll
@@ -365,7 +401,7 @@ __global__ __launch_bounds__(kF8Threads, 1) void fp8_gemm_kernel(
         const int row = 64 * wm + 32 * a + 8 * (i >> 2) + 4 * hl + (i & 3);
         if (FC == 1) {
           const float gt = acc[a][0][i], up = acc[a][1][i];
-          const float hv = __fdividef(gt, 1.0f + __expf(-gt)) * up;
+          const float hv = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;  // silu(gate) * up
           const uint32_t hb = __float_as_uint(hv);
           // MXFP8 over the 32 columns of this row held by the 32 lanes of this half-wave
           uint32_t m = hb & 0x7FFFFFFFu;

@@ -87,14 +87,29 @@ __device__ __forceinline__ uint32_t bf16_to_e4m3_scaled(uint32_t b, int shared) 
   return sgn | e4m3_mag_rne(M, E0 - shared);
 }
 
-// e4m3fn byte of fp32 bits b times 2^-shared (finite b).
+// e4m3fn byte of fp32 bits b times 2^-shared (finite b, shared in [-127, 127]), rounded to
+// nearest even and saturated at 448: the same function as e4m3_mag_rne of the exact value, in
+// a branch-free form for the FP8 GEMM's epilogue (it runs once per output).  The magnitude is
+// normalised (fp32 subnormals included), rescaled by adjusting its exponent (below 2^-126 the
+// result is 0, above 2^127 it saturates), clamped to 448; a normal e4m3 result is the fp32 value
+// rounded to 3 mantissa bits by an integer add, a subnormal one the count of 2^-9 units that an
+// fp32 add of 2^14 leaves (rounded to nearest even by the add).  Checked equal to e4m3_mag_rne
+// for every finite fp32 input and every shared exponent.
 __device__ __forceinline__ uint32_t f32_to_e4m3_scaled(uint32_t b, int shared) {
   const uint32_t sgn = (b >> 24) & 0x80u, mag = b & 0x7FFFFFFFu;
-  if (mag == 0) return sgn;
-  const uint32_t eb = mag >> 23, mb = mag & 0x7FFFFFu;
-  const uint32_t M = eb ? (mb | 0x800000u) : mb;
-  const int E0 = eb ? (int)eb - 150 : -149;
-  return sgn | e4m3_mag_rne(M, E0 - shared);
+  const uint32_t ein = mag >> 23;
+  const int lz = __clz((int)mag) - 8;  // 1 .. 23 for an fp32 subnormal
+  const int eeff = ein ? (int)ein : 1 - lz;
+  const uint32_t mant = ein ? (mag & 0x7FFFFFu) : ((mag << (lz & 31)) & 0x7FFFFFu);
+  const int E = eeff - shared;         // biased fp32 exponent of |b| * 2^-shared
+  const bool tiny = mag == 0 || E <= 0;
+  const int Ec = E < 1 ? 1 : (E > 254 ? 254 : E);
+  const float x = fminf(__uint_as_float(((uint32_t)Ec << 23) | mant), 448.0f);
+  uint32_t r = __float_as_uint(x);
+  r += 0x7FFFFu + ((r >> 20) & 1u);
+  const uint32_t nrm = ((((r >> 23) - 120u) << 3) | ((r >> 20) & 7u)) & 0xFFu;
+  const uint32_t sub = __float_as_uint(x + 16384.0f) - __float_as_uint(16384.0f);
+  return sgn | (tiny ? 0u : (x >= 0.015625f ? nrm : sub));
 }
 
 }  // namespace bitmoe
