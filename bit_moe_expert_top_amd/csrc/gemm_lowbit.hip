@@ -336,7 +336,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
         const size_t r = (size_t)(r0 + row);
         if constexpr (FC == 1) {
           const float gt = acc[m][0][j], up = acc[m][1][j];
-          const float hv = __fdividef(gt, 1.0f + __expf(-gt)) * up;
+          const float hv = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;  // silu(gate) * up
           reinterpret_cast<uint16_t*>(out)[r * width + 32 * (8 * nt_i + w) + F::pos32(i32)] =
               (uint16_t)f32_to_bf16_rne(hv);
         } else {
