@@ -154,21 +154,6 @@ hipError_t launch_mxfp4_to_fp8(const uint8_t* codes, const uint8_t* scales, int6
   return hipGetLastError();
 }
 
-// Maximum over the 32 lanes of each half-wave, in every lane: DPP exchanges within rows of 16
-// (xor 1, xor 2, half-row mirror, row mirror), then one ds_swizzle across the two rows of the
-// half-wave (bit mode: xor 16) -- instead of five ds_bpermute round trips.
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
-}
-__device__ __forceinline__ uint32_t half_wave_max_u32(uint32_t v) {
-  v = max(v, dpp_u32<0xB1>(v));   // quad_perm [1,0,3,2]
-  v = max(v, dpp_u32<0x4E>(v));   // quad_perm [2,3,0,1]
-  v = max(v, dpp_u32<0x141>(v));  // row_half_mirror
-  v = max(v, dpp_u32<0x140>(v));  // row_mirror
-  return max(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (0x10 << 10) | 0x1F));
-}
-
 // ------------------------------------------------------------------ FP8 grouped GEMM
 constexpr int kF8BM = 128, kF8BN = 256, kF8BK = 128, kF8Threads = 512;
 // One K step of the workgroup tile in LDS: A (token) and B (weight) rows of 128 bytes whose
@@ -342,11 +327,16 @@ __global__ __launch_bounds__(kF8Threads, 1) void fp8_gemm_kernel(
     // The MFMA builtins are pure, so the optimizer may sink them past the barriers and reads
     // that follow (and keep every operand live until then): an empty volatile asm that reads the
     // accumulators keeps each sub-step's MFMAs where they are issued.
+    // FC1 takes the weight tile as the matrix cores' A operand, so that a lane's 16 results are
+    // 16 channels of one token row (the MXFP8 block of h is then 16 values in each of two lanes);
+    // FC2 keeps the token tile as A (a lane holds one column of 16 rows of y).
     auto mfma_sub = [&](const F8Sub& o) {
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = mfma_scale_32x32x64_fp8(o.a[a], o.b[b], acc[a][b], o.sa[a], o.sb[b]);
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = FC == 1 ? mfma_scale_32x32x64_fp8(o.b[b], o.a[a], acc[a][b], o.sb[b], o.sa[a])
+                              : mfma_scale_32x32x64_fp8(o.a[a], o.b[b], acc[a][b], o.sa[a], o.sb[b]);
       asm volatile("" ::"v"(acc[0][0]), "v"(acc[0][1]), "v"(acc[1][0]), "v"(acc[1][1]));
     };
 
@@ -394,31 +384,45 @@ __global__ __launch_bounds__(kF8Threads, 1) void fp8_gemm_kernel(
     __syncthreads();
 
     // ---- epilogue
+    if (FC == 1) {
+      // acc[a][0] (gate) and acc[a][1] (up), element v: token row 64 wm + 32 a + r32 of the
+      // tile, channel 128 nt + 32 wn + 8 (v / 4) + 4 hl + v % 4.  The channels 128 nt + 32 wn +
+      // [0, 32) are one MXFP8 block of h, held by lanes r32 and r32 + 32.
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
+      for (int a = 0; a < 2; ++a) {
+        float hv[16];
+        uint32_t m = 0;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 64 * wm + 32 * a + 8 * (i >> 2) + 4 * hl + (i & 3);
-        if (FC == 1) {
-          const float gt = acc[a][0][i], up = acc[a][1][i];
-          const float hv = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;  // silu(gate) * up
-          const uint32_t hb = __float_as_uint(hv);
-          // MXFP8 over the 32 columns of this row held by the 32 lanes of this half-wave
-          uint32_t m = hb & 0x7FFFFFFFu;
-          m = half_wave_max_u32(m);
-          const int shared = mx_shared_exp(m ? floor_log2_f32(m) : 0, m == 0);
-          const uint32_t e = f32_to_e4m3_scaled(hb, shared);
+        for (int v = 0; v < 16; ++v) {
+          const float gt = acc[a][0][v], up = acc[a][1][v];
+          hv[v] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;  // silu(gate) * up
+          m = max(m, __float_as_uint(hv[v]) & 0x7FFFFFFFu);
+        }
+        m = max(m, (uint32_t)__shfl_xor((int)m, 32));
+        const int shared = mx_shared_exp(m ? floor_log2_f32(m) : 0, m == 0);
+        const int row = 64 * wm + 32 * a + r32;
+        if (row < nrows) {
+          const int64_t r = (int64_t)(r0 + row);
+          const int c0 = 128 * nt_i + 32 * wn;
+          uint32_t* dst = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(out) + r * width + c0 + 4 * hl);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            dst[2 * q] = e4m3x4_scaled(hv[4 * q], hv[4 * q + 1], hv[4 * q + 2], hv[4 * q + 3], shared);
+          if (hl == 0) out_scale[r * (width / 32) + c0 / 32] = (uint8_t)(shared + 127);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = 64 * wm + 32 * a + 8 * (i >> 2) + 4 * hl + (i & 3);
           if (row < nrows) {
             const int64_t r = (int64_t)(r0 + row);
-            const int col = 128 * nt_i + 32 * wn + r32;
-            reinterpret_cast<uint8_t*>(out)[r * width + col] = (uint8_t)e;
-            if (r32 == 0) out_scale[r * (width / 32) + col / 32] = (uint8_t)(shared + 127);
-          }
-        } else if (row < nrows) {
-          const int64_t r = (int64_t)(r0 + row);
 #pragma unroll
-          for (int b = 0; b < 2; ++b)
-            reinterpret_cast<float*>(out)[r * width + kF8BN * nt_i + 64 * wn + 32 * b + r32] = acc[a][b][i];
+            for (int b = 0; b < 2; ++b)
+              reinterpret_cast<float*>(out)[r * width + kF8BN * nt_i + 64 * wn + 32 * b + r32] = acc[a][b][i];
+          }
         }
       }
     }

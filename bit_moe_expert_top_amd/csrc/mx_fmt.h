@@ -87,29 +87,18 @@ __device__ __forceinline__ uint32_t bf16_to_e4m3_scaled(uint32_t b, int shared) 
   return sgn | e4m3_mag_rne(M, E0 - shared);
 }
 
-// e4m3fn byte of fp32 bits b times 2^-shared (finite b, shared in [-127, 127]), rounded to
-// nearest even and saturated at 448: the same function as e4m3_mag_rne of the exact value, in
-// a branch-free form for the FP8 GEMM's epilogue (it runs once per output).  The magnitude is
-// normalised (fp32 subnormals included), rescaled by adjusting its exponent (below 2^-126 the
-// result is 0, above 2^127 it saturates), clamped to 448; a normal e4m3 result is the fp32 value
-// rounded to 3 mantissa bits by an integer add, a subnormal one the count of 2^-9 units that an
-// fp32 add of 2^14 leaves (rounded to nearest even by the add).  Checked equal to e4m3_mag_rne
-// for every finite fp32 input and every shared exponent.
-__device__ __forceinline__ uint32_t f32_to_e4m3_scaled(uint32_t b, int shared) {
-  const uint32_t sgn = (b >> 24) & 0x80u, mag = b & 0x7FFFFFFFu;
-  const uint32_t ein = mag >> 23;
-  const int lz = __clz((int)mag) - 8;  // 1 .. 23 for an fp32 subnormal
-  const int eeff = ein ? (int)ein : 1 - lz;
-  const uint32_t mant = ein ? (mag & 0x7FFFFFu) : ((mag << (lz & 31)) & 0x7FFFFFu);
-  const int E = eeff - shared;         // biased fp32 exponent of |b| * 2^-shared
-  const bool tiny = mag == 0 || E <= 0;
-  const int Ec = E < 1 ? 1 : (E > 254 ? 254 : E);
-  const float x = fminf(__uint_as_float(((uint32_t)Ec << 23) | mant), 448.0f);
-  uint32_t r = __float_as_uint(x);
-  r += 0x7FFFFu + ((r >> 20) & 1u);
-  const uint32_t nrm = ((((r >> 23) - 120u) << 3) | ((r >> 20) & 7u)) & 0xFFu;
-  const uint32_t sub = __float_as_uint(x + 16384.0f) - __float_as_uint(16384.0f);
-  return sgn | (tiny ? 0u : (x >= 0.015625f ? nrm : sub));
+// Four e4m3fn bytes (v0 in the low byte) of fp32 values times 2^-shared (finite values,
+// shared in [-127, 127]), rounded to nearest even and saturated at 448.  gfx950's fp8
+// conversion (OCP e4m3fn, round to nearest even) of the value scaled by ldexp -- exact for every
+// result at or above 2^-126, and anything smaller rounds to zero either way -- and clamped to
+// +-448 first.  Checked on the device equal to e4m3_mag_rne of the exact value for every finite
+// fp32 input and every shared exponent.
+__device__ __forceinline__ float e4m3_prescale(float v, int shared) {
+  return __builtin_amdgcn_fmed3f(__builtin_amdgcn_ldexpf(v, -shared), 448.0f, -448.0f);
+}
+__device__ __forceinline__ uint32_t e4m3x4_scaled(float v0, float v1, float v2, float v3, int shared) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prescale(v0, shared), e4m3_prescale(v1, shared), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prescale(v2, shared), e4m3_prescale(v3, shared), lo, true);
 }
 
 }  // namespace bitmoe

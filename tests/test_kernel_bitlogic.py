@@ -291,16 +291,6 @@ def bf16_to_e4m3_scaled(b, shared):
     return sgn | e4m3_mag_rne(M, E0 - shared)
 
 
-def f32_to_e4m3_scaled(b, shared):
-    sgn, mag = (b >> 24) & 0x80, b & 0x7FFFFFFF
-    if mag == 0:
-        return sgn
-    eb, mb = mag >> 23, mag & 0x7FFFFF
-    M = (mb | 0x800000) if eb else mb
-    E0 = eb - 150 if eb else -149
-    return sgn | e4m3_mag_rne(M, E0 - shared)
-
-
 def test_integer_e4m3_encoder_matches_oracle_rne():
     r = np.random.default_rng(6)
     # bf16 patterns over the whole range (normals, subnormals, zeros), with shared exponents
@@ -311,14 +301,3 @@ def test_integer_e4m3_encoder_matches_oracle_rne():
     want = OF.e4m3fn_encode(vals)
     got = np.array([bf16_to_e4m3_scaled(int(b), int(s)) for b, s in zip(bits, shared)], np.uint8)
     np.testing.assert_array_equal(got, want)
-    # fp32 patterns near the rounding boundaries of e4m3 (ties, saturation, subnormals)
-    grid = OF.e4m3fn_value(np.arange(0, 0x7F, dtype=np.uint8))
-    mids = np.concatenate([(grid[:-1] + grid[1:]) / 2, grid, [448.0, 464.0, 465.0, 479.0, 480.0, 1e4]])
-    mids = np.concatenate([mids, -mids])
-    f32 = mids.astype(np.float32)
-    for shared in (-3, 0, 5):
-        v = f32.astype(np.float64) * 2.0 ** shared
-        v32 = v.astype(np.float32)
-        want = OF.e4m3fn_encode(v32.astype(np.float64) / 2.0 ** shared)
-        got = np.array([f32_to_e4m3_scaled(int(b), shared) for b in v32.view(np.uint32)], np.uint8)
-        np.testing.assert_array_equal(got, want)
