@@ -193,11 +193,18 @@ struct F8Sub {
 // its second register set and then issues stage kb's MFMAs: the LDS reads of the next step run
 // while the matrix cores work on this one.  The 128 x 256 tile reads 384 bytes of operands from
 // L2 per k for 64 K MACs.
+// The ring runs on across a workgroup's tasks: the last three steps of a task load the first
+// three stages of the next one (whose perm entries were fetched when the task began), so the
+// next task starts on stages already in LDS while this one's epilogue runs.  Every step issues
+// exactly 7 direct loads per wave (a step with nothing left to load re-reads the last stage,
+// which nobody reads), which is what the vmcnt(7) of each step's wait counts on.
 //   FC1: A = MXFP8 x rows gathered by perm / ktop; B = W1 image of the slot (rows [0, 2I));
 //        column tile n: wave column wn holds gate rows 128n + 32wn + [0,32) and up rows
 //        I + 128n + 32wn + [0,32); epilogue h = silu(gate) * up, MXFP8 per 32 columns -> hq.
 //   FC2: A = hq rows r0 ..; B = W2 image (rows [0, H)); epilogue y (fp32).
-template <int FC>
+// MODE = (K / 128) % 3 when K / 128 >= 3 (it fixes the ring buffer of every step at compile
+// time), 3 for K / 128 < 3 (no prefetch across tasks).
+template <int FC, int MODE>
 __global__ __launch_bounds__(kF8Threads, 1) void fp8_gemm_kernel(
     const int32_t* __restrict__ plan, int b0, int S, const uint8_t* __restrict__ slots,
     int64_t slot_bytes, int64_t w_off, int64_t ws_off, int rows_per_expert, int K, int width,
@@ -217,173 +224,241 @@ __global__ __launch_bounds__(kF8Threads, 1) void fp8_gemm_kernel(
   const int n_ntiles = FC == 1 ? width / (kF8BN / 2) : rows_per_expert / kF8BN;
   const int total = n_items * n_ntiles;
   const int nk = K / kF8BK, kb32 = K / 32;
+  // direct loads: round u of wave w fills LDS bytes [1024 (8u + w), +1024) of a tile, i.e.
+  // rows 8 (8u + w) + lane / 8, position lane % 8, which holds chunk (lane % 8) ^ ((row / 2) % 8)
+  const int prow = lane >> 3, ppos = lane & 7;
+  // scale loads (4 bytes per lane = one row's four e8m0 scales of the step): waves 0, 1 the A
+  // rows 64w + lane, waves 2..5 the B rows 64(w - 2) + lane, waves 6, 7 nothing (kOffNone)
+  const bool a_side = wu < 2;
+  const int sdst = kF8TileA + kF8TileB + 256 * w;  // LDS offset of this wave's scale load
 
-  for (int task = blockIdx.x; task < total; task += gridDim.x) {
-    const int item = task / n_ntiles, nt_i = task - item * n_ntiles;
+  // first task at or after t (stride gridDim.x) whose expert has a slot in this batch, or total
+  auto next_task = [&](int t) {
+    for (; t < total; t += gridDim.x) {
+      const int sl = items[t / n_ntiles].w - b0;
+      if (sl >= 0 && sl < S) break;
+    }
+    return t;
+  };
+  // B rows of the tile (LDS row j -> weight row) of column tile nt
+  auto wrow_of = [&](int nt, int j) {
+    if (FC == 1) {
+      const int jw = j >> 6, jj = j & 63;
+      return jj < 32 ? 128 * nt + 32 * jw + jj : width + 128 * nt + 32 * jw + (jj - 32);
+    }
+    return kF8BN * nt + j;
+  };
+
+  // The task whose stages are being loaded: its buffer resources and this lane's offsets.
+  buf_rsrc ra, ras, rb, rbs;
+  uint32_t aoff[2], boff[4], soff;
+  // A task: index, column tile, first grouped row, rows, slot; for FC1 also the perm entries of
+  // this lane's two A rows and of its scale row (loaded by every lane, clamped into the item).
+  struct Task {
+    int t, nt, r0, nrows, slot;
+    int praw[3];
+  };
+  auto begin = [&](Task& T, int t) {
+    const int item = t / n_ntiles;
     const int4 itm = items[item];
-    const int slot = itm.w - b0;
-    if (slot < 0 || slot >= S) continue;  // uniform over the block
-    const int r0 = itm.y, nrows = itm.z;
-    const uint8_t* img = slots + (int64_t)slot * slot_bytes;
-
-    // direct loads: round u of wave w fills LDS bytes [1024 (8u + w), +1024) of a tile, i.e.
-    // rows 8 (8u + w) + lane / 8, position lane % 8, which holds chunk (lane % 8) ^ ((row / 2) % 8)
-    const int prow = lane >> 3, ppos = lane & 7;
-    const buf_rsrc ra = FC == 1 ? make_rsrc(asrc, (uint32_t)(a_rows * K))
-                                : make_rsrc(asrc + (int64_t)r0 * K, (uint32_t)nrows * K);
-    const buf_rsrc ras = FC == 1 ? make_rsrc(ascale, (uint32_t)(a_rows * kb32))
-                                 : make_rsrc(ascale + (int64_t)r0 * kb32, (uint32_t)nrows * kb32);
-    uint32_t aoff[2];
+    T.t = t;
+    T.nt = t - item * n_ntiles;
+    T.r0 = itm.y;
+    T.nrows = itm.z;
+    T.slot = itm.w - b0;
+    if (FC == 1) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) T.praw[u] = perm[T.r0 + min(8 * (8 * u + w) + prow, T.nrows - 1)];
+      T.praw[2] = perm[T.r0 + min(64 * (w & 1) + lane, T.nrows - 1)];
+    }
+  };
+  // makes T the task being loaded
+  auto finish = [&](const Task& T) {
+    const uint8_t* img = slots + (int64_t)T.slot * slot_bytes;
+    rb = make_rsrc(img + w_off, (uint32_t)rows_per_expert * K);
+    rbs = make_rsrc(img + ws_off, (uint32_t)rows_per_expert * kb32);
+    if (FC == 1) {
+      ra = make_rsrc(asrc, (uint32_t)(a_rows * K));
+      ras = make_rsrc(ascale, (uint32_t)(a_rows * kb32));
+    } else {
+      ra = make_rsrc(asrc + (int64_t)T.r0 * K, (uint32_t)T.nrows * K);
+      ras = make_rsrc(ascale + (int64_t)T.r0 * kb32, (uint32_t)T.nrows * kb32);
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int r = 8 * (8 * u + w) + prow;
-      aoff[u] = kOffNone;
-      if (r < nrows) {
-        const uint32_t arow = FC == 1 ? (uint32_t)(perm[r0 + r] / ktop) : (uint32_t)r;
-        aoff[u] = arow * (uint32_t)K + 16u * (uint32_t)(ppos ^ ((r >> 1) & 7));
-      }
+      const uint32_t arow = FC == 1 ? (uint32_t)(T.praw[u] / ktop) : (uint32_t)r;
+      aoff[u] = r < T.nrows ? arow * (uint32_t)K + 16u * (uint32_t)(ppos ^ ((r >> 1) & 7)) : kOffNone;
     }
-    // B rows of the tile (LDS row j -> weight row)
-    auto wrow_of = [&](int j) {
-      if (FC == 1) {
-        const int jw = j >> 6, jj = j & 63;
-        return jj < 32 ? 128 * nt_i + 32 * jw + jj : width + 128 * nt_i + 32 * jw + (jj - 32);
-      }
-      return kF8BN * nt_i + j;
-    };
-    const buf_rsrc rb = make_rsrc(img + w_off, (uint32_t)rows_per_expert * K);
-    const buf_rsrc rbs = make_rsrc(img + ws_off, (uint32_t)rows_per_expert * kb32);
-    uint32_t boff[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int j = 8 * (8 * u + w) + prow;
-      boff[u] = (uint32_t)wrow_of(j) * K + 16u * (uint32_t)(ppos ^ ((j >> 1) & 7));
+      boff[u] = (uint32_t)wrow_of(T.nt, j) * K + 16u * (uint32_t)(ppos ^ ((j >> 1) & 7));
     }
-    // scale loads (4 bytes per lane = one row's four e8m0 scales of the step): waves 0, 1 the A
-    // rows 64w + lane, waves 2..5 the B rows 64(w - 2) + lane, waves 6, 7 nothing (kOffNone)
-    const bool a_side = wu < 2;
-    uint32_t soff = kOffNone;
+    soff = kOffNone;
     if (w < 2) {
       const int r = 64 * w + lane;
-      if (r < nrows) soff = (FC == 1 ? (uint32_t)(perm[r0 + r] / ktop) : (uint32_t)r) * (uint32_t)kb32;
+      if (r < T.nrows) soff = (FC == 1 ? (uint32_t)(T.praw[2] / ktop) : (uint32_t)r) * (uint32_t)kb32;
     } else if (w < 6) {
-      soff = (uint32_t)wrow_of(64 * (w - 2) + lane) * (uint32_t)kb32;
+      soff = (uint32_t)wrow_of(T.nt, 64 * (w - 2) + lane) * (uint32_t)kb32;
     }
-    // LDS offset of this wave's scale load within a stage
-    const int sdst = kF8TileA + kF8TileB + 256 * w;
+  };
 
-    auto stage_ptr = [&](int s) -> uint8_t* { return s == 0 ? st0 : (s == 1 ? st1 : st2); };
-    // the loads of step kb (clamped to the last step: the copies past the end are never read)
-    // into stage buffer s
-    auto load_stage = [&](int s, int kb) {
-      uint8_t* st = stage_ptr(s);
-      const uint32_t ko = (uint32_t)min(kb, nk - 1) * kF8BK;
+  auto stage_ptr = [&](int s) -> uint8_t* { return s == 0 ? st0 : (s == 1 ? st1 : st2); };
+  // the loads of step kb of the task being loaded into stage buffer s
+  auto load_stage = [&](int s, int kb) {
+    uint8_t* st = stage_ptr(s);
+    const uint32_t ko = (uint32_t)kb * kF8BK;
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds8_void*)(st + 1024 * (8 * u + wu)), 16, (int)aoff[u],
-                                                 (int)ko, 0, 0);
+    for (int u = 0; u < 2; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds8_void*)(st + 1024 * (8 * u + wu)), 16, (int)aoff[u],
+                                               (int)ko, 0, 0);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds8_void*)(st + kF8TileA + 1024 * (8 * u + wu)), 16,
-                                                 (int)boff[u], (int)ko, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_side ? ras : rbs, (lds8_void*)(st + sdst), 4, (int)soff,
-                                               (int)(ko / 32), 0, 0);
-    };
-    // this wave's operands of sub-step kk of a step from stage buffer s.  Tile rows 64 wm + 32 t
-    // + r32 have (row / 2) % 8 == (r32 / 2) % 8, so the swizzled position of chunk c is the same
-    // for every tile: per lane four chunk offsets (c = hl, 2 + hl, 4 + hl, 6 + hl) and a row base,
-    // the rest are instruction offsets.
-    uint32_t cofs[4];
+    for (int u = 0; u < 4; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds8_void*)(st + kF8TileA + 1024 * (8 * u + wu)), 16,
+                                               (int)boff[u], (int)ko, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(a_side ? ras : rbs, (lds8_void*)(st + sdst), 4, (int)soff,
+                                             (int)(ko / 32), 0, 0);
+  };
+  // this wave's operands of sub-step kk of a step from stage buffer s.  Tile rows 64 wm + 32 t
+  // + r32 have (row / 2) % 8 == (r32 / 2) % 8, so the swizzled position of chunk c is the same
+  // for every tile: per lane four chunk offsets (c = hl, 2 + hl, 4 + hl, 6 + hl) and a row base,
+  // the rest are instruction offsets.
+  uint32_t cofs[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) cofs[j] = 16u * (uint32_t)((2 * j + hl) ^ ((r32 >> 1) & 7));
-    const uint32_t abase = 128u * (uint32_t)(64 * wm + r32), bbase = 128u * (uint32_t)(64 * wn + r32);
-    const uint32_t sabase = 4u * (uint32_t)(64 * wm + r32) + hl, sbbase = 4u * (uint32_t)(64 * wn + r32) + hl;
-    auto read_sub = [&](F8Sub& o, int s, int kk) {
-      const uint8_t* la = stage_ptr(s);
-      const uint8_t* lb = la + kF8TileA;
-      const uint8_t* lsa = lb + kF8TileB;
-      const uint8_t* lsb = lsa + kF8SclA;
+  for (int j = 0; j < 4; ++j) cofs[j] = 16u * (uint32_t)((2 * j + hl) ^ ((r32 >> 1) & 7));
+  const uint32_t abase = 128u * (uint32_t)(64 * wm + r32), bbase = 128u * (uint32_t)(64 * wn + r32);
+  const uint32_t sabase = 4u * (uint32_t)(64 * wm + r32) + hl, sbbase = 4u * (uint32_t)(64 * wn + r32) + hl;
+  auto read_sub = [&](F8Sub& o, int s, int kk) {
+    const uint8_t* la = stage_ptr(s);
+    const uint8_t* lb = la + kF8TileA;
+    const uint8_t* lsa = lb + kF8TileB;
+    const uint8_t* lsb = lsa + kF8SclA;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(la + abase + cofs[2 * kk] + 4096 * t);
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(la + abase + cofs[2 * kk + 1] + 4096 * t);
-        const u32x4 b0_ = *reinterpret_cast<const u32x4*>(lb + bbase + cofs[2 * kk] + 4096 * t);
-        const u32x4 b1_ = *reinterpret_cast<const u32x4*>(lb + bbase + cofs[2 * kk + 1] + 4096 * t);
-        o.a[t] = i32x8_t{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-        o.b[t] = i32x8_t{(int)b0_[0], (int)b0_[1], (int)b0_[2], (int)b0_[3], (int)b1_[0], (int)b1_[1], (int)b1_[2],
-                         (int)b1_[3]};
-        o.sa[t] = lsa[sabase + 128 * t + 2 * kk];
-        o.sb[t] = lsb[sbbase + 128 * t + 2 * kk];
-      }
-    };
+    for (int t = 0; t < 2; ++t) {
+      const u32x4 a0 = *reinterpret_cast<const u32x4*>(la + abase + cofs[2 * kk] + 4096 * t);
+      const u32x4 a1 = *reinterpret_cast<const u32x4*>(la + abase + cofs[2 * kk + 1] + 4096 * t);
+      const u32x4 b0_ = *reinterpret_cast<const u32x4*>(lb + bbase + cofs[2 * kk] + 4096 * t);
+      const u32x4 b1_ = *reinterpret_cast<const u32x4*>(lb + bbase + cofs[2 * kk + 1] + 4096 * t);
+      o.a[t] = i32x8_t{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+      o.b[t] = i32x8_t{(int)b0_[0], (int)b0_[1], (int)b0_[2], (int)b0_[3], (int)b1_[0], (int)b1_[1], (int)b1_[2],
+                       (int)b1_[3]};
+      o.sa[t] = lsa[sabase + 128 * t + 2 * kk];
+      o.sb[t] = lsb[sbbase + 128 * t + 2 * kk];
+    }
+  };
 
-    f32x16_t acc[2][2];
+  f32x16_t acc[2][2];
+  // The MFMA builtins are pure, so the optimizer may sink them past the barriers and reads
+  // that follow (and keep every operand live until then): an empty volatile asm that reads the
+  // accumulators keeps each sub-step's MFMAs where they are issued.
+  // FC1 takes the weight tile as the matrix cores' A operand, so that a lane's 16 results are
+  // 16 channels of one token row (the MXFP8 block of h is then 16 values in each of two lanes);
+  // FC2 keeps the token tile as A (a lane holds one column of 16 rows of y).
+  auto mfma_sub = [&](const F8Sub& o) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        acc[a][b] = FC == 1 ? mfma_scale_32x32x64_fp8(o.b[b], o.a[a], acc[a][b], o.sb[b], o.sa[a])
+                            : mfma_scale_32x32x64_fp8(o.a[a], o.b[b], acc[a][b], o.sa[a], o.sb[b]);
+    asm volatile("" ::"v"(acc[0][0]), "v"(acc[0][1]), "v"(acc[1][0]), "v"(acc[1][1]));
+  };
+
+  const int t_first = next_task(blockIdx.x);
+  if (t_first >= total) return;  // uniform over the block
+  Task cur, nxt;
+  begin(cur, t_first);
+  finish(cur);
+
+  // Step kb (stage kb in buffer D; sub-step 0's operands already in s0):
+  //   read sub-step 1 into s1; MFMAs of sub-step 0;
+  //   wait for this wave's loads of stage kb+1 and its reads of stage kb; barrier: stage kb+1
+  //   is complete and nobody reads buffer D any more; load stage kl of the task being loaded
+  //   into D (kb+3 of this task, 0..2 of the next one, or a copy of the last stage);
+  //   read sub-step 0 of step kb+1 into s0 (unless kb is the last step); MFMAs of sub-step 1.
+  F8Sub s0, s1;
+  auto step = [&](auto D_, int kb, int kl, bool read_next) {
+    constexpr int D = decltype(D_)::value;
+    read_sub(s1, D, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_sub(s0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((kF8Loads & 15) | 0x70 | ((kF8Loads >> 4) << 14));  // vmcnt(7), lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+    load_stage(D, kl);
+    if (read_next) read_sub(s0, (D + 1) % 3, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_sub(s1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  // the first three stages of the task being loaded into buffers P, P+1, P+2, then the wait for
+  // stage 0 (every wave)
+  auto prologue = [&](auto P_) {
+    constexpr int P = decltype(P_)::value;
+    load_stage(P, 0);
+    load_stage((P + 1) % 3, min(1, nk - 1));
+    load_stage((P + 2) % 3, min(2, nk - 1));
+    __builtin_amdgcn_s_waitcnt((2 * kF8Loads & 15) | 0x70 | 0xF00 | (((2 * kF8Loads) >> 4) << 14));  // vmcnt(14)
+    asm volatile("s_barrier" ::: "memory");
+  };
+  // The K loop of the current task (K / 128 >= 3), its stage 0 in buffer P and already in LDS:
+  // steps whose kb+3 is still in the task, then three steps that load the next task's stages
+  // 0..2 (pf) or copies.
+  auto run = [&](auto P_, bool pf) {
+    constexpr int P = decltype(P_)::value;
+    using IP0 = std::integral_constant<int, P>;
+    using IP1 = std::integral_constant<int, (P + 1) % 3>;
+    using IP2 = std::integral_constant<int, (P + 2) % 3>;
+    constexpr int Q = (P + MODE) % 3;  // buffer of the first of the last three steps
+    using IQ0 = std::integral_constant<int, Q>;
+    using IQ1 = std::integral_constant<int, (Q + 1) % 3>;
+    using IQ2 = std::integral_constant<int, (Q + 2) % 3>;
+    read_sub(s0, P, 0);
+    int kb = 0;
+    for (; kb + 6 <= nk; kb += 3) {
+      step(IP0{}, kb, kb + 3, true);
+      step(IP1{}, kb + 1, kb + 4, true);
+      step(IP2{}, kb + 2, kb + 5, true);
+    }
+    if (MODE >= 1) step(IP0{}, kb, kb + 3, true);  // nk - 3 - kb == MODE steps remain before the last three
+    if (MODE >= 2) step(IP1{}, kb + 1, kb + 4, true);
+    kb = nk - 3;
+    if (pf) finish(nxt);  // the loads below are the next task's
+    step(IQ0{}, kb, pf ? 0 : nk - 1, true);
+    step(IQ1{}, kb + 1, pf ? 1 : nk - 1, true);
+    step(IQ2{}, kb + 2, pf ? 2 : nk - 1, false);
+  };
+  // K / 128 < 3: the task loads its own stages into buffers 0..2
+  auto run_small = [&]() {
+    prologue(I0{});
+    read_sub(s0, 0, 0);
+    step(I0{}, 0, nk - 1, nk > 1);
+    if (nk > 1) step(I1{}, 1, nk - 1, false);
+  };
+
+  // One task (its stage 0 in buffer P, or K / 128 < 3); returns false after the last one.
+  auto task = [&](auto P_) -> bool {
+    const int tn = next_task(cur.t + (int)gridDim.x);
+    const bool has_next = tn < total, pf = MODE < 3 && has_next;
+    if (has_next) begin(nxt, tn);
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
-    // The MFMA builtins are pure, so the optimizer may sink them past the barriers and reads
-    // that follow (and keep every operand live until then): an empty volatile asm that reads the
-    // accumulators keeps each sub-step's MFMAs where they are issued.
-    // FC1 takes the weight tile as the matrix cores' A operand, so that a lane's 16 results are
-    // 16 channels of one token row (the MXFP8 block of h is then 16 values in each of two lanes);
-    // FC2 keeps the token tile as A (a lane holds one column of 16 rows of y).
-    auto mfma_sub = [&](const F8Sub& o) {
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-          acc[a][b] = FC == 1 ? mfma_scale_32x32x64_fp8(o.b[b], o.a[a], acc[a][b], o.sb[b], o.sa[a])
-                              : mfma_scale_32x32x64_fp8(o.a[a], o.b[b], acc[a][b], o.sa[a], o.sb[b]);
-      asm volatile("" ::"v"(acc[0][0]), "v"(acc[0][1]), "v"(acc[1][0]), "v"(acc[1][1]));
-    };
-
-    // Step kb (stage kb in buffer D; sub-step 0's operands already in s0):
-    //   read sub-step 1 into s1; MFMAs of sub-step 0;
-    //   wait for this wave's loads of stage kb+1 and its reads of stage kb; barrier: stage kb+1
-    //   is complete and nobody reads buffer D any more; load stage kb+3 into D;
-    //   read sub-step 0 of step kb+1 into s0; MFMAs of sub-step 1.
-    F8Sub s0, s1;
-    auto step = [&](auto D_, int kb) {
-      constexpr int D = decltype(D_)::value;
-      read_sub(s1, D, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_sub(s0);
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt((kF8Loads & 15) | 0x70 | ((kF8Loads >> 4) << 14));  // vmcnt(7), lgkmcnt(0)
-      asm volatile("s_barrier" ::: "memory");
-      load_stage(D, kb + 3);
-      if (kb + 1 < nk) read_sub(s0, (D + 1) % 3, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_sub(s1);
-      __builtin_amdgcn_sched_barrier(0);
-    };
-
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    load_stage(0, 0);
-    load_stage(1, 1);
-    load_stage(2, 2);
-    __builtin_amdgcn_s_waitcnt((2 * kF8Loads & 15) | 0x70 | 0xF00 | (((2 * kF8Loads) >> 4) << 14));  // vmcnt(14)
-    asm volatile("s_barrier" ::: "memory");  // stage 0 is complete for every wave
-    read_sub(s0, 0, 0);
-    int kb = 0;
-    for (; kb + 3 <= nk; kb += 3) {
-      step(I0{}, kb);
-      step(I1{}, kb + 1);
-      step(I2{}, kb + 2);
-    }
-    if (kb < nk) step(I0{}, kb);  // 0, 1 or 2 steps remain, from buffer 0
-    if (kb + 1 < nk) step(I1{}, kb + 1);
-    // every wave is done with the stage buffers before the next task's loads (and the loads of
-    // stages past the end, which nobody reads, have landed)
-    __builtin_amdgcn_s_waitcnt(0xC07F & ~0xC00F);  // vmcnt(0), lgkmcnt(0)
-    __syncthreads();
+    if (MODE == 3)
+      run_small();
+    else
+      run(P_, pf);
+    // No LDS is read past the last step's barrier, so the next task's loads can land while the
+    // epilogue runs.
 
     // ---- epilogue
+    const int nt_i = cur.nt, r0 = cur.r0, nrows = cur.nrows;
     if (FC == 1) {
       // acc[a][0] (gate) and acc[a][1] (up), element v: token row 64 wm + 32 a + r32 of the
       // tile, channel 128 nt + 32 wn + 8 (v / 4) + 4 hl + v % 4.  The channels 128 nt + 32 wn +
@@ -426,7 +501,30 @@ __global__ __launch_bounds__(kF8Threads, 1) void fp8_gemm_kernel(
         }
       }
     }
+    if (!has_next) return false;
+    cur = nxt;
+    if (!pf) finish(cur);
+    return true;
+  };
+
+  // With K / 128 = 3q + MODE the next task's stage 0 lands in buffer (P + MODE) % 3, so the
+  // tasks of a workgroup cycle through the buffers 0, MODE, 2 MODE (mod 3); the loop is unrolled
+  // over that cycle so that every step's buffers are known at compile time.
+  if (MODE == 3) {
+    while (task(I0{})) {
+    }
+  } else {
+    prologue(I0{});
+    constexpr int P1 = MODE % 3, P2 = (2 * MODE) % 3;
+    for (;;) {
+      if (!task(I0{})) break;
+      if (MODE == 0) continue;
+      if (!task(std::integral_constant<int, P1>{})) break;
+      if (!task(std::integral_constant<int, P2>{})) break;
+    }
   }
+  // the loads past the end (copies of the last stage) land before the workgroup's LDS is freed
+  __builtin_amdgcn_s_waitcnt(0xC07F & ~0xC00F);  // vmcnt(0), lgkmcnt(0)
 }
 
 // ------------------------------------------------------------------ launchers
@@ -466,8 +564,19 @@ static hipError_t launch_fp8(const int32_t* plan, int b0, int S, const uint8_t* 
                              hipStream_t s) {
   const int64_t cap = 256;  // one workgroup per CU
   const int grid = (int)(tasks < cap ? (tasks > 0 ? tasks : 1) : cap);
-  fp8_gemm_kernel<FC><<<grid, kF8Threads, 0, s>>>(plan, b0, S, slots, slot_bytes, w_off, ws_off, rows, K,
-                                                width, ktop, asrc, ascale, perm, a_rows, out, out_scale);
+  const int nk = K / kF8BK;
+  auto go = [&](auto kern) {
+    kern<<<grid, kF8Threads, 0, s>>>(plan, b0, S, slots, slot_bytes, w_off, ws_off, rows, K, width, ktop, asrc,
+                                     ascale, perm, a_rows, out, out_scale);
+  };
+  if (nk < 3)
+    go(fp8_gemm_kernel<FC, 3>);
+  else if (nk % 3 == 0)
+    go(fp8_gemm_kernel<FC, 0>);
+  else if (nk % 3 == 1)
+    go(fp8_gemm_kernel<FC, 1>);
+  else
+    go(fp8_gemm_kernel<FC, 2>);
   return hipGetLastError();
 }
 

@@ -20,7 +20,7 @@ import moegen
 from oracle import formats as OF
 from oracle import moe as OM
 
-from _helpers import device_layer, host, layer_arrays, oracle_layer, to_dev
+from _helpers import device_layer, fp8_h_bound, host, layer_arrays, oracle_layer, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -115,9 +115,7 @@ def test_fp8_slot_image_bit_exact(L, fp8_slots):
 
 def _hq_oracle(lay, x_bits, k, I, rows, perm, offsets):
     """The oracle's h (fp64) for the given grouped rows of hot experts -- x quantised to MXFP8,
-    FC1 with the expert's FP8 image, SwiGLU -- and a first-order bound of how far a computation
-    whose FC1 sums carry an error of at most KAPPA * sqrt(sum of squared products) can move h:
-    |dh| <= |silu'(g)| |u| dg + |silu(g)| du."""
+    FC1 with the expert's FP8 image, SwiGLU -- and the bound dh of fp8_h_bound."""
     X = OF.bf16_value(x_bits)
     Xq = OF.mxfp8_dequant(*OF.mxfp8_quantize(X))
     expert_of = np.searchsorted(offsets, rows, side="right") - 1
@@ -125,15 +123,7 @@ def _hq_oracle(lay, x_bits, k, I, rows, perm, offsets):
     dh = np.zeros((len(rows), I))
     for e in sorted(set(expert_of.tolist())):
         sel = np.nonzero(expert_of == e)[0]
-        xs = Xq[perm[rows[sel]] // k]
-        W1 = lay.dense(e, 1)
-        a = OM.fc1(xs, W1)
-        s = np.sqrt(OM.fc1(xs * xs, W1 * W1))
-        g, u = a[:, :I], a[:, I:]
-        sig = 1.0 / (1.0 + np.exp(-g))
-        h[sel] = OM.swiglu(a)
-        dsilu = sig * (1.0 + g * (1.0 - sig))
-        dh[sel] = KAPPA * (np.abs(dsilu * u) * s[:, :I] + np.abs(g * sig) * s[:, I:])
+        h[sel], dh[sel] = fp8_h_bound(Xq[perm[rows[sel]] // k], lay.dense(e, 1))
     return h, dh
 
 
@@ -147,7 +137,6 @@ def _hq_oracle(lay, x_bits, k, I, rows, perm, offsets):
 # deviation measured) of the values that round to the GPU's element.  A block scale may differ only where the oracle's amax lies within dh of a
 # power of two, and on at most 1e-4 of the blocks.
 HQ_RATE = 1e-3
-KAPPA = 1e-3
 
 
 def _e4m3_grid():
