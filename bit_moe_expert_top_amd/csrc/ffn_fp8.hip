@@ -494,9 +494,12 @@ __global__ __launch_bounds__(kF8Threads, 1) void fp8_gemm_kernel(
           const int row = 64 * wm + 32 * a + 8 * (i >> 2) + 4 * hl + (i & 3);
           if (row < nrows) {
             const int64_t r = (int64_t)(r0 + row);
+            // y is read once, by the combine: non-temporal stores keep it from displacing the
+            // weights and h in the caches (FC2 -5 % at 32K rows)
 #pragma unroll
             for (int b = 0; b < 2; ++b)
-              reinterpret_cast<float*>(out)[r * width + kF8BN * nt_i + 64 * wn + 32 * b + r32] = acc[a][b][i];
+              __builtin_nontemporal_store(acc[a][b][i],
+                                          reinterpret_cast<float*>(out) + r * width + kF8BN * nt_i + 64 * wn + 32 * b + r32);
           }
         }
       }

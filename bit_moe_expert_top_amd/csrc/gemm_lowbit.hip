@@ -340,10 +340,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
           reinterpret_cast<uint16_t*>(out)[r * width + 32 * (8 * nt_i + w) + F::pos32(i32)] =
               (uint16_t)f32_to_bf16_rne(hv);
         } else {
+          // y is read once, by the combine: non-temporal stores (FC2 -3 % at T=8192)
 #pragma unroll
           for (int c = 0; c < NCT; ++c)
-            reinterpret_cast<float*>(out)[r * width + 256 * NCT * nt_i + 32 * NCT * w + 32 * c + i32] =
-                acc[m][c][j];
+            __builtin_nontemporal_store(acc[m][c][j], reinterpret_cast<float*>(out) + r * width +
+                                                          256 * NCT * nt_i + 32 * NCT * w + 32 * c + i32);
         }
       }
     }
