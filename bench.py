@@ -294,7 +294,7 @@ def measure(sp: dict, dw, T: int, steps: int, warmup: int, flush_between: bool =
         f = 2.0 * hot_rows * (2 * I) * H
         roof_ms = hot_fc1_ms / hot_batches
         achieved = f / hot_batches / (roof_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": "moe_expert_ffn hot FP8 FC1 + SwiGLU + MXFP8 of h (fp8_gemm_kernel<1>)",
+        roof = {"bound": "mfma", "kernel": "moe_expert_ffn hot FP8 FC1 + SwiGLU + MXFP8 of h (fp8_gemm_kernel<1, MODE>)",
                 "achieved": achieved, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / FP8_PEAK_TFLOPS, "alg_flops_per_launch": f / hot_batches, "hot_rows": hot_rows}
     elif gemm:
