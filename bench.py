@@ -182,8 +182,9 @@ def measure(sp: dict, dw, T: int, steps: int, warmup: int, flush_between: bool =
     # stream, concurrent with the low-bit stages
     side = torch.cuda.Stream() if sp["n_hot"] > 0 else None
 
-    # small batches: routing, grouping and the FFN's preparation (stage 0) in one launch
-    front = side is None and T <= L.FRONT_MAX_T
+    # decode-sized batches: routing, grouping and the FFN's preparation (stage 0) in one call
+    # (one launch up to 16 tokens, two above)
+    front = side is None and T * k <= L.FRONT_MAX_ROWS
 
     def step(evs=None):
         if evs:
@@ -351,7 +352,7 @@ def measure(sp: dict, dw, T: int, steps: int, warmup: int, flush_between: bool =
         "step_timing": "HIP graph replay" if graph_ms else "eager launches",
         "ms_per_step_eager": eager_ms,
         "hot_convert_overlapped": side is not None,
-        "front_one_launch": front,  # moe_route_permute_prepare instead of route + permute + stage 0
+        "front_call": front,  # moe_route_permute_prepare instead of route + permute + stage 0
         "stages_ms": {"route+permute+prepare+combine (eager; stage sum for one stream)": eager_ms - fc1_ms - fc2_ms - conv_ms - hot_fc1_ms - hot_fc2_ms,
                       "fc1": fc1_ms, "fc2": fc2_ms, "hot_convert": conv_ms, "hot_fc1": hot_fc1_ms, "hot_fc2": hot_fc2_ms},
         "ffn_stage_ms": [float(np.mean(v)) for v in stage_ms],

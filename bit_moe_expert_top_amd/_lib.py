@@ -249,12 +249,12 @@ def moe_expert_ffn_two_streams(w: DeviceWeights, x: torch.Tensor, k: int, counts
     return y_perm
 
 
-FRONT_MAX_T = 16  # moe_route_permute_prepare takes batches of at most this many tokens
+FRONT_MAX_ROWS = 4096  # moe_route_permute_prepare takes batches of at most this many routed rows (T*k)
 
 
 def moe_route_permute_prepare(w: DeviceWeights, logits: torch.Tensor, x: torch.Tensor, k: int, ws: torch.Tensor,
                               out=None):
-    """moe_route + moe_permute + stage 0 of the FFN in one launch (T <= FRONT_MAX_T); returns
+    """moe_route + moe_permute + stage 0 of the FFN (T*k <= FRONT_MAX_ROWS); returns
     (topk_ids, topk_w, counts, offsets, perm, inv).  ``ws`` is the FFN workspace."""
     _dev(logits, torch.float32, "logits")
     T, E = logits.shape

@@ -385,7 +385,7 @@ moe_status moe_route_permute_prepare(const moe_weights* w, const float* logits, 
   if (st != MOE_OK) return st;
   if (T < 0 || k < 1 || k > w->E || k > kMaxTopK) return MOE_ERR_INVALID_ARG;
   if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
-  if (T > kFrontMaxT) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)T * k > kPermuteChunk) return MOE_ERR_UNSUPPORTED;  // one workgroup groups the rows
   hipStream_t s = as_stream(stream);
   if (T == 0) {  // as moe_permute: counts and offsets all zero; nothing else to do
     hipError_t e1 = launch_fill_i32(counts, w->E, 0, s);

@@ -51,9 +51,10 @@ hipError_t launch_prepare(const int32_t* offsets, int E, int small_max, int gemm
                           int32_t* plan_g, const uint16_t* x, int T, int H, int fmt, uint16_t* xp,
                           hipStream_t s);
 
-// Routing, grouping and stage 0 of the FFN in one launch (front.hip), for T <= kFrontMaxT and
-// R = T*k <= kPermuteChunk.  nchunks and nbits are set by launch_front.
-constexpr int kFrontMaxT = 16;
+// Routing, grouping and stage 0 of the FFN (front.hip) for R = T*k <= kPermuteChunk: one launch
+// for T <= kFrontOneLaunchT, else the route kernel and then one launch for the rest.  nchunks and
+// nbits are set by launch_front.
+constexpr int kFrontOneLaunchT = 16;
 struct FrontArgs {
   const float* logits;
   int T, E, k, nbits;

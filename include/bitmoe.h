@@ -210,16 +210,17 @@ moe_status moe_expert_ffn_stage(const moe_weights* w, const uint16_t* x, int32_t
                                 void* stream);
 
 /* moe_route_permute_prepare -- moe_route, moe_permute and stage 0 of moe_expert_ffn in one
- * launch, for small batches: a decode step is a chain of short kernels whose fixed start and
- * drain costs add up, and the pages capture their decode step in a graph for that reason
- * ([Moet-README] README tables, graph-captured decode).  Same arguments as those three calls
+ * launch for up to 16 tokens, in two (routing, then the rest) for up to R = T*k = 4096 rows:
+ * a decode step is a chain of short kernels whose fixed start and drain costs add up, and the
+ * pages capture their decode step in a graph for that reason ([Moet-README] README tables,
+ * graph-captured decode).  Same arguments as those three calls
  * (topk_ids i32[T][k], topk_w f32[T][k], counts i32[E], offsets i32[E+1], perm i32[R],
  * inv i32[R], the FFN workspace ws of moe_expert_ffn_ws_bytes); the outputs and the workspace
  * contents are bit-equal to moe_route + moe_permute + moe_expert_ffn_stage(..., 0, ...), so
  * stages 1 .. n-1 of moe_expert_ffn_stage then complete the FFN.  All pointers are device
  * pointers owned by the caller; the call only enqueues on `stream`.
  * Errors: INVALID_ARG (bad weights, T < 0, k out of [1, min(E, 64)], null pointers),
- * UNSUPPORTED for T > 16 (use the three calls), WORKSPACE as moe_expert_ffn.  T = 0 fills
+ * UNSUPPORTED for T*k > 4096 (use the three calls), WORKSPACE as moe_expert_ffn.  T = 0 fills
  * counts and offsets with zeros, as moe_permute does. */
 moe_status moe_route_permute_prepare(const moe_weights* w, const float* logits, const uint16_t* x,
                                      int32_t T, int32_t k, int32_t* topk_ids, float* topk_w,

@@ -158,8 +158,8 @@ def test_quantizer_argument_checks(lib):
 
 
 def test_front_argument_checks(lib):
-    """moe_route_permute_prepare rejects bad arguments on the host; batches above 16 tokens are
-    UNSUPPORTED (the caller runs the three calls instead)."""
+    """moe_route_permute_prepare rejects bad arguments on the host; batches above 4096 routed
+    rows (T*k) are UNSUPPORTED (the caller runs the three calls instead)."""
     import sys
     sys.path.insert(0, ROOT)
     from bit_moe_expert_top_amd import _lib as L
@@ -169,7 +169,8 @@ def test_front_argument_checks(lib):
     f = L.lib.moe_route_permute_prepare
     args = lambda T, k, ws_bytes=1 << 30, counts=p: (ctypes.byref(w), p, p, T, k, p, p, counts, p, p, p, p,
                                                       ws_bytes, None)
-    assert f(*args(17, 2)) == -2                 # more than 16 tokens: not this call
+    assert f(*args(2049, 2)) == -2               # more than 4096 rows: not this call
+    assert f(*args(2048, 2, ws_bytes=10)) == -3  # 4096 rows pass; the workspace is checked next
     assert f(*args(4, 0)) == -1                  # k < 1
     assert f(*args(4, 9)) == -1                  # k > E
     assert f(*args(-1, 2)) == -1                 # T < 0

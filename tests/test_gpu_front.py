@@ -1,5 +1,5 @@
-"""GPU: moe_route_permute_prepare (routing, grouping and the FFN's preparation in one launch)
-gives the same bits as moe_route + moe_permute + stage 0 of moe_expert_ffn: the ids, gates,
+"""GPU: moe_route_permute_prepare (routing, grouping and the FFN's preparation in one launch up to
+16 tokens, in two above: the route kernel, then the rest) gives the same bits as moe_route + moe_permute + stage 0 of moe_expert_ffn: the ids, gates,
 counts, offsets, perm and inv, the whole FFN workspace after the preparation, and the layer
 output once stages 1 .. n-1 and the combine have run.  The three-call path is checked against the
 oracle by the parity tests at these layers and sizes."""
@@ -36,7 +36,13 @@ def _rest(L, dw, x, k, counts, offsets, perm, inv, gw, ws, T):
 @pytest.mark.parametrize("name,T,override", [("tiny", 1, {}), ("tiny", 16, {}), ("decode", 1, {}),
                                              ("decode", 3, {}), ("decode", 8, {}), ("decode", 16, {}),
                                              ("w3", 1, {}), ("w3", 16, {}), ("residual", 8, {}),
-                                             ("mixed", 5, MIXED_SMALL), ("mixed", 16, {})])
+                                             ("mixed", 5, MIXED_SMALL), ("mixed", 16, {}),
+                                             # two launches: 17 tokens, the decode batch, the
+                                             # grouped-GEMM list (T >= 128), the largest batch
+                                             # (R = T*k = 4096 rows)
+                                             ("tiny", 100, {}), ("decode", 17, {}), ("decode", 64, {}),
+                                             ("decode", 128, {}), ("decode", 512, {}), ("w3", 64, {}),
+                                             ("residual", 64, {}), ("mixed", 64, MIXED_SMALL)])
 def test_front_equals_three_calls(L, name, T, override):
     sp, dw = device_layer(name, **override)
     k = sp["k"]
