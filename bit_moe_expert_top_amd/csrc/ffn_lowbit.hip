@@ -153,24 +153,26 @@ __device__ __forceinline__ void wait_vmcnt() {
 //      the next super-step's codes and scales (issued after B(st)) may stay in flight -- then
 //      a barrier: B(st) of every wave is in LDS and every wave is done with B(st-1);
 //   2. issue B(st+1) into the other stage; at S = 0 then issue the codes and scales of
-//      super-step c+1; decode + MFMA, the token operands read one operand ahead of their
-//      MFMAs (the LDS latency hides behind the decode).
-template <class F, int NT, int G, int CS, int BS, int S>
+//      super-step c+1 (not in the last super-step, LAST, whose S = 1 step then waits for
+//      everything); decode + MFMA, the token operands read one operand ahead of their MFMAs
+//      (the LDS latency hides behind the decode).
+template <class F, int NT, int G, int CS, int BS, int S, bool LAST>
 __device__ __forceinline__ void step(Pipe<F, NT, G>& P, f32x4 (&acc)[kRT][NT], buf_rsrc rb, uint8_t* bs0,
                                      uint8_t* bs1, const uint32_t* doff, uint32_t active, int wu,
                                      const uint32_t* bread, int c, int n_it) {
   constexpr int kLc = F::kStepCodeBytes > 16 ? 2 : 1;  // load instructions per tile and step
-  constexpr int kAfter = S == 1 ? kRT * (1 + G * kLc) : 0;
+  constexpr int kAfter = S == 1 && !LAST ? kRT * (1 + G * kLc) : 0;
   const int st = G * c + S;
   wait_vmcnt<kAfter>();
   __syncthreads();
   if (st + 1 < n_it) dma_b<G>(rb, BS ? bs0 : bs1, doff, active, wu, st + 1);
   if constexpr (S == 0) {
-    const int n_ss = n_it / G;
 #pragma unroll
     for (int t = 0; t < kRT; ++t) P.sc[t] = P.sc_next[t];
-    load_scales<F, NT, G>(P, min(c + 1, n_ss - 1));
-    load_codes<F, NT, G>(P, CS ^ 1, min(c + 1, n_ss - 1));
+    if constexpr (!LAST) {
+      load_scales<F, NT, G>(P, c + 1);
+      load_codes<F, NT, G>(P, CS ^ 1, c + 1);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   const uint8_t* bsrc = BS ? bs1 : bs0;
@@ -199,27 +201,33 @@ __device__ __forceinline__ void step(Pipe<F, NT, G>& P, f32x4 (&acc)[kRT][NT], b
 }
 
 // One super-step c (code ring slot CS = c % 2).
-template <class F, int NT, int G, int CS>
+template <class F, int NT, int G, int CS, bool LAST>
 __device__ __forceinline__ void superstep(Pipe<F, NT, G>& P, f32x4 (&acc)[kRT][NT], buf_rsrc rb, uint8_t* bs0,
                                           uint8_t* bs1, const uint32_t* doff, uint32_t active, int wu,
                                           const uint32_t* bread, int c, int n_it) {
   // B stage of step G*c + S is its parity: S for G = 2, CS for G = 1
-  step<F, NT, G, CS, (G == 1 ? CS : 0), 0>(P, acc, rb, bs0, bs1, doff, active, wu, bread, c, n_it);
-  if constexpr (G == 2) step<F, NT, G, CS, 1, 1>(P, acc, rb, bs0, bs1, doff, active, wu, bread, c, n_it);
+  step<F, NT, G, CS, (G == 1 ? CS : 0), 0, LAST>(P, acc, rb, bs0, bs1, doff, active, wu, bread, c, n_it);
+  if constexpr (G == 2) step<F, NT, G, CS, 1, 1, LAST>(P, acc, rb, bs0, bs1, doff, active, wu, bread, c, n_it);
 }
 
-// The super-steps of one pass (the prologue's loads of super-step 0 and of B(0) issued).
+// The super-steps of one pass (the prologue's loads of super-step 0 and of B(0) issued).  The
+// last one is peeled off the loop: it loads no next super-step.
 template <class F, int NT, int G>
 __device__ __forceinline__ void stream_loop(Pipe<F, NT, G>& P, f32x4 (&acc)[kRT][NT], buf_rsrc rb, uint8_t* bs0,
                                             uint8_t* bs1, const uint32_t* doff, uint32_t active, int wu,
                                             const uint32_t* bread, int n_it) {
-  const int n_ss = n_it / G;
+  const int n_ss = n_it / G;  // >= 1
   int c = 0;
-  for (; c + 1 < n_ss; c += 2) {
-    superstep<F, NT, G, 0>(P, acc, rb, bs0, bs1, doff, active, wu, bread, c, n_it);
-    superstep<F, NT, G, 1>(P, acc, rb, bs0, bs1, doff, active, wu, bread, c + 1, n_it);
+  for (; c + 2 < n_ss; c += 2) {
+    superstep<F, NT, G, 0, false>(P, acc, rb, bs0, bs1, doff, active, wu, bread, c, n_it);
+    superstep<F, NT, G, 1, false>(P, acc, rb, bs0, bs1, doff, active, wu, bread, c + 1, n_it);
   }
-  if (c < n_ss) superstep<F, NT, G, 0>(P, acc, rb, bs0, bs1, doff, active, wu, bread, c, n_it);
+  if (c + 2 == n_ss) {
+    superstep<F, NT, G, 0, false>(P, acc, rb, bs0, bs1, doff, active, wu, bread, c, n_it);
+    superstep<F, NT, G, 1, true>(P, acc, rb, bs0, bs1, doff, active, wu, bread, c + 1, n_it);
+  } else {
+    superstep<F, NT, G, 0, true>(P, acc, rb, bs0, bs1, doff, active, wu, bread, c, n_it);
+  }
 }
 
 // Source offsets of this lane's direct B loads (one per 256-chunk round u of the workgroup) for
