@@ -42,8 +42,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   if (OUT_F32) {
     reinterpret_cast<float4*>((float*)out + (size_t)t * H)[c] = acc;
   } else {
-    const uint32_t lo = f32_to_bf16_rne(acc.x) | (f32_to_bf16_rne(acc.y) << 16);
-    const uint32_t hi = f32_to_bf16_rne(acc.z) | (f32_to_bf16_rne(acc.w) << 16);
+    const uint32_t lo = f32x2_to_bf16x2_rne(acc.x, acc.y);
+    const uint32_t hi = f32x2_to_bf16x2_rne(acc.z, acc.w);
     reinterpret_cast<uint2*>((uint16_t*)out + (size_t)t * H)[c] = make_uint2(lo, hi);
   }
 }

@@ -487,20 +487,21 @@ __global__ __launch_bounds__(kF8Threads, 1) void fp8_gemm_kernel(
         }
       }
     } else {
+      // y through a buffer resource that spans the item's nrows rows: the rows past the item
+      // are dropped by its bound (no test per value).  y is read once, by the combine:
+      // non-temporal stores (aux bit 1) keep it from displacing the weights and h in the caches
+      // (FC2 -5 % at 32K rows)
+      const buf_rsrc ro = make_rsrc(reinterpret_cast<float*>(out) + (int64_t)r0 * width,
+                                    (uint32_t)nrows * (uint32_t)width * 4u);
+      const uint32_t vo = ((uint32_t)(64 * wm + 4 * hl) * (uint32_t)width + (uint32_t)(kF8BN * nt_i + 64 * wn + r32)) * 4u;
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int row = 64 * wm + 32 * a + 8 * (i >> 2) + 4 * hl + (i & 3);
-          if (row < nrows) {
-            const int64_t r = (int64_t)(r0 + row);
-            // y is read once, by the combine: non-temporal stores keep it from displacing the
-            // weights and h in the caches (FC2 -5 % at 32K rows)
+          const uint32_t off = vo + (uint32_t)(32 * a + 8 * (i >> 2) + (i & 3)) * (uint32_t)width * 4u;
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
-              __builtin_nontemporal_store(acc[a][b][i],
-                                          reinterpret_cast<float*>(out) + r * width + kF8BN * nt_i + 64 * wn + 32 * b + r32);
-          }
+          for (int b = 0; b < 2; ++b)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[a][b][i]), ro, (int)(off + 128u * b), 0, 2);
         }
       }
     }

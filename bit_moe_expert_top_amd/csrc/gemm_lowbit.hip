@@ -411,25 +411,31 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
         step(std::integral_constant<int, 3>{}, kb + 3);
       }
 
-      // ---- epilogue: lane holds column i32 of each tile, rows 32m + 8(j/4) + 4hk + j%4
+      // ---- epilogue: lane holds column i32 of each tile, rows 32m + 8(j/4) + 4hk + j%4.  The
+      //      stores go through a buffer resource that spans the item's nrows rows, so the rows
+      //      past the item are dropped by its bound (no test per value); the lane's row 4hk and
+      //      column are in a base offset, the rest of the row is uniform.
+      constexpr uint32_t kEl = FC == 1 ? 2u : 4u;  // bytes per element: h bf16, y fp32
+      const buf_rsrc ro = make_rsrc(reinterpret_cast<uint8_t*>(out) + (size_t)r0 * width * kEl,
+                                    (uint32_t)nrows * (uint32_t)width * kEl);
+      const uint32_t col = FC == 1 ? (uint32_t)(32 * (8 * nt_i + w) + F::pos32(ti32))
+                                   : (uint32_t)(256 * NCT * nt_i + 32 * NCT * w + ti32);
+      const uint32_t vo = ((uint32_t)(4 * thk) * (uint32_t)width + col) * kEl;
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const int row = 32 * m + 8 * (j >> 2) + 4 * thk + (j & 3);
-          if (row >= nrows) continue;
-          const size_t r = (size_t)(r0 + row);
+          const uint32_t ro_off = vo + (uint32_t)(32 * m + 8 * (j >> 2) + (j & 3)) * (uint32_t)width * kEl;
           if constexpr (FC == 1) {
             const float gt = acc[m][0][j], up = acc[m][1][j];
             const float hv = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;  // silu(gate) * up
-            reinterpret_cast<uint16_t*>(out)[r * width + 32 * (8 * nt_i + w) + F::pos32(ti32)] =
-                (uint16_t)f32_to_bf16_rne(hv);
+            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16_rne(hv), ro, (int)ro_off, 0, 0);
           } else {
-            // y is read once, by the combine: non-temporal stores (FC2 -3 % at T=8192)
+            // y is read once, by the combine: non-temporal stores (aux bit 1; FC2 -3 % at T=8192)
 #pragma unroll
             for (int c = 0; c < NCT; ++c)
-              __builtin_nontemporal_store(acc[m][c][j], reinterpret_cast<float*>(out) + r * width +
-                                                            256 * NCT * nt_i + 32 * NCT * w + 32 * c + ti32);
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[m][c][j]), ro, (int)(ro_off + 32u * c * kEl), 0,
+                                                    2);
           }
         }
       }
