@@ -54,6 +54,51 @@ __device__ __forceinline__ void wave_range(int chunk_lo, int chunk_hi, int w, in
   *hi = min(chunk_hi, *lo + per);
 }
 
+// R <= 64 rows (a decode batch): wave 0 places them in registers -- a row's position in the
+// stable (id, row) order is the number of rows with a smaller id, found bit by bit from the most
+// significant one with one ballot per bit, plus the rows with its id on lower lanes -- and every
+// thread then counts, for its experts, the ids below and equal to it among the <= 64 kept in LDS.
+// No per-wave counters, no scans; the outputs are those of the general path (ids outside [0, E)
+// skipped).  keys: 64 ints of LDS.
+__device__ __forceinline__ void permute_small(const int32_t* ids, int R, int E, int nbits,
+                                              int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                              int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+                                              int32_t* keys, int32_t* off2) {
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    const int id = lane < R ? ids[lane] : E;
+    const bool ok = (unsigned)id < (unsigned)E;
+    const int key = ok ? id : E;  // E (the sentinel) sorts after every id and is never counted
+    keys[lane] = key;
+    const uint64_t cand = __ballot(ok);
+    uint64_t same = cand;  // rows whose id agrees with this row's above bit b
+    int below = 0;         // rows with a smaller id
+    for (int b = nbits - 1; b >= 0; --b) {
+      const int bit = (key >> b) & 1;
+      const uint64_t bal = __ballot(bit) & cand;
+      if (bit) below += __popcll(same & ~bal);
+      same &= bit ? bal : ~bal;
+    }
+    if (ok) {
+      const int pos = below + __popcll(same & ((1ull << lane) - 1ull));
+      perm[pos] = lane;
+      inv[lane] = pos;
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e <= E; e += kPermThreads) {
+    int lt = 0, eq = 0;
+    for (int r = 0; r < R; ++r) {
+      const int k = keys[r];
+      lt += k < e;
+      eq += k == e;
+    }
+    if (e < E) counts[e] = eq;
+    offsets[e] = lt;
+    if (off2) off2[e] = lt;
+  }
+}
+
 // Group R <= kPermuteChunk rows in one workgroup of kPermThreads threads: counts[E],
 // offsets[E+1], perm[R], inv[R] (global), and the offsets also into off2 if not null.
 // smem: kPermWaves * E + kPermThreads / 64 + 1 ints.
@@ -61,6 +106,10 @@ __device__ __forceinline__ void permute_block(const int32_t* ids, int R, int E, 
                                               int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                               int32_t* __restrict__ perm, int32_t* __restrict__ inv,
                                               int32_t* smem, int32_t* off2) {
+  if (R <= kWave) {
+    permute_small(ids, R, E, nbits, counts, offsets, perm, inv, smem, off2);
+    return;
+  }
   int32_t* cnt = smem;                        // [kPermWaves][E]
   int32_t* scan_tmp = smem + kPermWaves * E;  // kPermThreads/64 + 1
   const int w = threadIdx.x / kWave;
