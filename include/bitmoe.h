@@ -141,7 +141,10 @@ moe_status moe_route(const float* logits, int32_t T, int32_t E, int32_t k,
  *                         (expert, token, slot)
  *   inv      i32[R]       out: inv[perm[r]] = r
  *   ws       scratch of at least moe_permute_ws_bytes(T, k, E) bytes (may be NULL if that is 0)
- * The result is deterministic (no order-dependent atomics).
+ * The result is deterministic (no order-dependent atomics).  Rows whose id lies outside [0, E)
+ * are left out: counts and offsets count the other rows only (offsets[E] is their number), perm
+ * lists them first, and the inv entries of the left-out rows and the rest of perm are not
+ * written.
  * Errors: INVALID_ARG (bad sizes, null output, R >= 2^31), WORKSPACE (ws too small). */
 size_t moe_permute_ws_bytes(int32_t T, int32_t k, int32_t E);
 moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,

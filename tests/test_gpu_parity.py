@@ -72,6 +72,26 @@ def test_permute_bit_exact(L, T, E, k):
     np.testing.assert_array_equal(host(inv), wi)
 
 
+@pytest.mark.parametrize("T,E,k", [(5, 8, 8), (64, 384, 8), (700, 384, 8)])
+def test_permute_leaves_out_ids_outside_range(L, T, E, k):
+    """Rows whose id is outside [0, E) (here -1 and E + 3) are left out of the grouping: counts,
+    offsets and the first offsets[E] entries of perm are those of the other rows (stable by row),
+    and inv maps each of them back.  R = 40 (one wave), 512 (one workgroup), 5600 (several)."""
+    r = np.random.default_rng(77 + T)
+    ids = r.integers(0, E, size=(T, k)).astype(np.int32)
+    bad = r.uniform(size=(T, k)) < 0.1
+    ids[bad] = np.where(r.uniform(size=int(bad.sum())) < 0.5, -1, E + 3).astype(np.int32)
+    counts, offsets, perm, inv = L.moe_permute(to_dev(ids), E)
+    flat = ids.reshape(-1)
+    valid = np.flatnonzero((flat >= 0) & (flat < E))
+    order = valid[np.argsort(flat[valid], kind="stable")]
+    want_counts = np.bincount(flat[valid], minlength=E)
+    np.testing.assert_array_equal(host(counts), want_counts)
+    np.testing.assert_array_equal(host(offsets), np.concatenate([[0], np.cumsum(want_counts)]))
+    np.testing.assert_array_equal(host(perm)[:len(valid)], order)
+    np.testing.assert_array_equal(host(inv)[order], np.arange(len(valid)))
+
+
 def test_permute_empty_batch(L):
     ids = torch.zeros((0, 2), dtype=torch.int32, device="cuda")
     counts, offsets, perm, inv = L.moe_permute(ids, 8)
