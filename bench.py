@@ -305,7 +305,7 @@ def measure(sp: dict, dw, T: int, steps: int, warmup: int, flush_between: bool =
         fc1_flops = 2.0 * gemm_rows * (2 * I) * H
         roof_ms = float(np.mean(stage_ms[2]))
         achieved = fc1_flops / (roof_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": "moe_expert_ffn stage 2: FC1 + SwiGLU grouped GEMM (gemm_kernel<W2Fmt, 1, 2>)",
+        roof = {"bound": "mfma", "kernel": "moe_expert_ffn stage 2: FC1 + SwiGLU grouped GEMM (gemm_kernel<W2Fmt, 1, 2, 8>)",
                 "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / BF16_PEAK_TFLOPS, "alg_flops_per_launch": fc1_flops, "gemm_rows": gemm_rows}
     else:

@@ -6,12 +6,13 @@
 // along K.  [Strata-R9700] path 6: 3-bit codes on eight levels, an e4m3 scale / 64 per 64.
 //
 // Work item = (row tile of <= 128 grouped rows of one expert, column tile of the weight rows).
-// A workgroup has 8 waves; every wave computes all 128 rows x its own 32*NCT weight columns with
-// v_mfma_f32_32x32x16_bf16 (4 x NCT MFMA tiles; 2 x NCT for an item of at most 64 rows).  The weights never pass through LDS: each lane
+// A workgroup has WV waves (8; 4 for K of at most 512, two workgroups per CU); every wave
+// computes all 128 rows x its own 32*NCT weight columns with v_mfma_f32_32x32x16_bf16 (4 x NCT
+// MFMA tiles; 2 x NCT for an item of at most 64 rows).  The weights never pass through LDS: each lane
 // loads and decodes straight into its MFMA B registers the 32-k field it supplies (lane l:
 // weight row l % 32 of a column tile, k-half l / 32 of every 64-k step; for 2-bit codes that is
 // exactly one scale group), with the format's own decode (lowbit_fmt.h).  Only the token rows
-// (the A operand, shared by the 8 waves) are staged in LDS: direct global -> LDS loads into a
+// (the A operand, shared by the workgroup's waves) are staged in LDS: direct global -> LDS loads into a
 // four-deep ring, 16-byte chunks XOR-swizzled by row / 2 (conflict-free reads of 128-byte rows),
 // one barrier per 64-k step; the packed codes and scales run in a four-slot register ring; codes
 // are fetched two steps ahead, token rows three.  Per MFMA the LDS carries
@@ -25,10 +26,10 @@
 // starts without a prologue (its loads overlap the end of the K loop and the epilogue).
 // Token operand and decoded weights share the format's k-slot order: x comes permuted from the
 // prepare kernel and FC1 writes h permuted, so A and B always agree.
-//   FC1 column tile n (NCT = 2): wave w holds gate rows 256n + 32w + [0,32) and up rows
-//       I + 256n + 32w + [0,32) as its two MFMA column tiles, so gate and up of one h column sit
-//       in the same lane and register and SwiGLU is applied in the epilogue (h stored bf16).
-//   FC2 column tile n: weight rows 256*NCT*n + 32*NCT*w + 32c + [0,32) (NCT = 2 when H is a
+//   FC1 column tile n (NCT = 2): wave w holds gate rows 32WVn + 32w + [0,32) and up rows
+//       I + 32WVn + 32w + [0,32) as its two MFMA column tiles, so gate and up of one h column
+//       sit in the same lane and register and SwiGLU is applied in the epilogue (h stored bf16).
+//   FC2 column tile n: weight rows 32WV*NCT*n + 32*NCT*w + 32c + [0,32) (NCT = 2 when H is a
 //       multiple of 512, else 1); the epilogue stores y (fp32).
 #include <type_traits>
 
@@ -48,10 +49,10 @@ __device__ __forceinline__ f32x16 mfma_32x32x16_bf16(u32x4 a, u32x4 b, f32x16 c)
                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-constexpr int kBM = 128, kBK = 64, kThreads = 512;
+constexpr int kBM = 128, kBK = 64;
 constexpr int kAStage = kBM * kBK * 2;  // one step of token rows (bf16): 16 KB
 // token rows run in a ring of 4 stages (as0..as3): stage = step % 4, a static index
-constexpr int kGemmGrid = 256;          // one workgroup per CU, 32 per XCD
+constexpr int kGemmCUs = 256;           // workgroups per launch: 8 / WV per CU
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt not waited on)
@@ -83,12 +84,14 @@ __device__ __forceinline__ void load_field(Field<F>& g, buf_rsrc rc, buf_rsrc rs
     g.s = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, (int)so, 0, 0);
 }
 
-template <class F, int FC, int NCT>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
+template <class F, int FC, int NCT, int WV>
+__global__ __launch_bounds__(64 * WV, 8 / WV) void gemm_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int rows_per_expert,
     int K, int width, int ktop, const uint16_t* __restrict__ asrc, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ plan, uint32_t asrc_bytes, void* __restrict__ out) {
   static_assert(FC == 2 || NCT == 2, "FC1 pairs a gate and an up column tile per wave");
+  static_assert(WV == 4 || WV == 8, "8 waves per workgroup, or 4 (two workgroups per CU)");
+  constexpr int kU = 16 / WV;  // 8-row token loads per wave and step (128 rows over WV waves)
   // one __shared__ object per stage: the compiler tracks the direct-to-LDS loads per object, so a
   // read of one stage waits only for that stage's loads (one array would wait for all of them)
   __shared__ __align__(16) uint8_t as0[kAStage];
@@ -106,7 +109,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
   const int i32 = lane & 31, hk = lane >> 5;
   const int n_items = plan[0];
   const int4* items = reinterpret_cast<const int4*>(plan + 4);
-  const int n_ntiles = FC == 1 ? width / 256 : rows_per_expert / (256 * NCT);
+  const int n_ntiles = FC == 1 ? width / (32 * WV) : rows_per_expert / (32 * WV * NCT);
   const uint32_t cbr = F::code_bytes((uint32_t)K), sbr = F::scale_bytes((uint32_t)K);
   const int nk = K / kBK;  // a multiple of 4 (K is a multiple of 256)
   // XCD-aware order: item blocks b = x, x + 8, ... go to XCD x (blockIdx % 8, for a grid that
@@ -150,26 +153,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
   // task they are switched to the next one (below), whose first loads then overlap the end of
   // this task's K loop and its epilogue.
   buf_rsrc ra, rc, rs;
-  uint32_t aoff[2], coff[NCT], soff[NCT];
-  // ---- token rows (A): wave w loads rows 16w + 8u + lane/8 (u = 0, 1), 16-byte chunk
+  uint32_t aoff[kU], coff[NCT], soff[NCT];
+  // ---- token rows (A): wave w loads rows (128/WV)w + 8u + lane/8 (u < 16/WV), 16-byte chunk
   //      position lane % 8 <- source chunk (lane % 8) ^ ((row / 2) % 8).  FC1 gathers rows of x (all
   //      of x is addressable); FC2 reads h rows r0.. of the item (based at r0: h may reach 2 GiB)
-  auto arow_of = [&](int u) { return 16 * w + 8 * u + (lane >> 3); };
+  auto arow_of = [&](int u) { return (128 / WV) * w + 8 * u + (lane >> 3); };
   // the source row of this lane's two A rows of task t: FC1 issues the perm loads here (branch
   // free, rows past the item clamped into it), read by set_rows
-  auto row_lookup = [&](const Task& t, uint32_t(&tok)[2]) {
+  auto row_lookup = [&](const Task& t, uint32_t(&tok)[kU]) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < kU; ++u) {
       const int rr = min(arow_of(u), t.nrows - 1);
       tok[u] = FC == 1 ? (uint32_t)perm[t.r0 + rr] : (uint32_t)rr;
     }
   };
   constexpr bool kGroup = F::kId == W2Fmt::kId;
   if constexpr (FC == 1) ra = make_rsrc(asrc, asrc_bytes);  // all of x, for every task
-  auto set_rows = [&](const Task& t, const uint32_t(&tok)[2]) {
+  auto set_rows = [&](const Task& t, const uint32_t(&tok)[kU]) {
     if constexpr (FC == 2) ra = make_rsrc(asrc + (size_t)t.r0 * K, (uint32_t)t.nrows * K * 2u);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < kU; ++u) {
       const int ar = arow_of(u);
       const uint32_t rowx = FC == 1 ? tok[u] / (uint32_t)ktop : tok[u];
       const int pos = lane & 7, src = pos ^ ((ar >> 1) & 7);
@@ -190,8 +193,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     rs = make_rsrc(scales + ebase * sbr, (uint32_t)rows_per_expert * sbr);
 #pragma unroll
     for (int c = 0; c < NCT; ++c) {
-      const int wrow = FC == 1 ? (c == 0 ? 256 * t.nt_i + 32 * w + i32 : width + 256 * t.nt_i + 32 * w + i32)
-                               : 256 * NCT * t.nt_i + 32 * NCT * w + 32 * c + i32;
+      const int wrow = FC == 1 ? (c == 0 ? 32 * WV * t.nt_i + 32 * w + i32 : width + 32 * WV * t.nt_i + 32 * w + i32)
+                               : 32 * WV * NCT * t.nt_i + 32 * NCT * w + 32 * c + i32;
       if constexpr (kGroup) {
         coff[c] = (uint32_t)wrow * cbr + F::code_bytes(128u * hk);
         soff[c] = (uint32_t)wrow * sbr + F::scale_bytes(128u * hk);
@@ -240,8 +243,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
   auto dma_a = [&](auto T_, int kb) {
     uint8_t* st = stage_ptr(T_);
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(st + 1024 * (2 * wu + u)), 16,
+    for (int u = 0; u < kU; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(st + 1024 * (kU * wu + u)), 16,
                                                (int)(aoff[u] + 2u * kstep(kb)), 0, 0, 0);
   };
 
@@ -249,7 +252,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
   // rows of steps 0..2; then the wait for step 0 and a barrier.
   constexpr int kPrologueCodeLoads = kGroup ? kGroupLoads : 2 * NCT * field_loads<F>();
   auto prologue = [&](const Task& t) {
-    uint32_t tok[2];
+    uint32_t tok[kU];
     row_lookup(t, tok);
     set_weights(t);
     if constexpr (kGroup) {
@@ -263,7 +266,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     dma_a(std::integral_constant<int, 0>{}, 0);
     dma_a(std::integral_constant<int, 1>{}, min(1, nk - 1));
     dma_a(std::integral_constant<int, 2>{}, min(2, nk - 1));
-    gemm_wait_vmcnt<4>();  // the first codes and the token rows of step 0 (steps 1, 2 may fly)
+    gemm_wait_vmcnt<2 * kU>();  // the first codes and the token rows of step 0 (steps 1, 2 may fly)
     asm volatile("s_barrier" ::: "memory");
   };
 
@@ -329,7 +332,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
       const int ng = nk >> 2;
       auto step = [&](auto S8_, int kb) {
         constexpr int S8 = decltype(S8_)::value, S = S8 & 3, P = S8 >> 2;
-        constexpr int kWait = 2 + (kGroup && S == 1 ? kGroupLoads : 0);
+        constexpr int kWait = kU + (kGroup && S == 1 ? kGroupLoads : 0);
         const uint8_t* st = stage_ptr(std::integral_constant<int, S>{});
         const uint8_t* sn = stage_ptr(std::integral_constant<int, (S + 1) & 3>{});
         const uint32_t* fw[NCT];
@@ -386,7 +389,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
       int kb = 0;
       for (; kb + 8 <= nk; kb += 8) {
         const bool hand = pipe && kb + 8 == nk;
-        uint32_t tok_n[2] = {0u, 0u};
+        uint32_t tok_n[kU] = {};
         step(std::integral_constant<int, 0>{}, kb);
         step(std::integral_constant<int, 1>{}, kb + 1);
         step(std::integral_constant<int, 2>{}, kb + 2);
@@ -418,8 +421,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
       constexpr uint32_t kEl = FC == 1 ? 2u : 4u;  // bytes per element: h bf16, y fp32
       const buf_rsrc ro = make_rsrc(reinterpret_cast<uint8_t*>(out) + (size_t)r0 * width * kEl,
                                     (uint32_t)nrows * (uint32_t)width * kEl);
-      const uint32_t col = FC == 1 ? (uint32_t)(32 * (8 * nt_i + w) + F::pos32(ti32))
-                                   : (uint32_t)(256 * NCT * nt_i + 32 * NCT * w + ti32);
+      const uint32_t col = FC == 1 ? (uint32_t)(32 * (WV * nt_i + w) + F::pos32(ti32))
+                                   : (uint32_t)(32 * WV * NCT * nt_i + 32 * NCT * w + ti32);
       const uint32_t vo = ((uint32_t)(4 * thk) * (uint32_t)width + col) * kEl;
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
@@ -451,7 +454,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
       // steps, before this epilogue's stores): wait for its codes of step 0 (3-bit: steps 0, 1
       // come one per step) and its rows of step 0, then a barrier.  Its step 0 refills the stage of
       // this task's last step only after the barrier of its own step 0.
-      gemm_wait_vmcnt<kGroup ? 4 : 4 + NCT * field_loads<F>()>();
+      gemm_wait_vmcnt<kGroup ? 2 * kU : 2 * kU + NCT * field_loads<F>()>();
       asm volatile("s_barrier" ::: "memory");
     } else {
       // every wave is done reading the token stages before the prologue refills them: an
@@ -466,13 +469,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
   gemm_wait_vmcnt<0>();
 }
 
+// Short K (at most 8 steps of 64, e.g. FC2 of a layer with I = 512): two 4-wave workgroups per
+// CU, whose barriers are independent, so one's task start and epilogue overlap the other's
+// MFMAs (3-bit FC2 at I = 512: -13 %); longer K: one 8-wave workgroup per CU, which loads each
+// item's token rows once for twice the columns (prefill FC1 and FC2 +5 % on 4 waves).
+template <class F, int FC, int NCT, int WV>
+static hipError_t launch_gemm_wv(const void* codes, const void* scales, int rows, int K, int width,
+                                 int ktop, const uint16_t* asrc, const int32_t* perm,
+                                 const int32_t* plan, uint32_t asrc_bytes, void* out, hipStream_t s) {
+  gemm_kernel<F, FC, NCT, WV><<<kGemmCUs * 8 / WV, 64 * WV, 0, s>>>(
+      (const uint8_t*)codes, (const uint8_t*)scales, rows, K, width, ktop, asrc, perm, plan, asrc_bytes, out);
+  return hipGetLastError();
+}
 template <class F, int FC, int NCT>
 static hipError_t launch_gemm(const void* codes, const void* scales, int rows, int K, int width,
                               int ktop, const uint16_t* asrc, const int32_t* perm,
                               const int32_t* plan, uint32_t asrc_bytes, void* out, hipStream_t s) {
-  gemm_kernel<F, FC, NCT><<<kGemmGrid, kThreads, 0, s>>>((const uint8_t*)codes, (const uint8_t*)scales, rows,
-                                                         K, width, ktop, asrc, perm, plan, asrc_bytes, out);
-  return hipGetLastError();
+  return K <= 8 * kBK ? launch_gemm_wv<F, FC, NCT, 4>(codes, scales, rows, K, width, ktop, asrc, perm, plan, asrc_bytes, out, s)
+                      : launch_gemm_wv<F, FC, NCT, 8>(codes, scales, rows, K, width, ktop, asrc, perm, plan, asrc_bytes, out, s);
 }
 
 hipError_t launch_lowbit_gemm_fc1(const LowbitWeights& w, int H, int I, int k, const uint16_t* xp,
