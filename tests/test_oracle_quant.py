@@ -1,7 +1,6 @@
 """Pins of the oracle's quantisers (oracle/quant.py) against brute force, closed forms and
 invariants that do not reuse its own formulas."""
 import numpy as np
-import pytest
 
 from oracle import formats as F
 from oracle import quant as Q
